@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark: one CP4 rank's share of a 16,384-token packed budget on one MI355X.
+
+A step is one pass of the whole per-rank hot path on the share's inputs (already
+resident in HBM): for each of the 4 KV chunks, host planning + plan upload +
+the attention kernel (cpattn_fwd_chunk), and after each chunk but the first the
+LSE merge (cpattn_merge) into the running result.  `value` is the share's
+algorithmic causal FLOPs (4 * D * Hq per visible query/key pair) divided by the
+step time.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload cp4_share] [--seed 0]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "causal attn TFLOP/s + MFMA util%, 16K-token THD pack at CP4-share, 1 GPU"
+BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+
+
+def visible_pairs(cu_q, cu_k, q_off, k_off) -> int:
+    """Visible (query, key) pairs per head under the causal mask, closed form per sequence."""
+    total = 0
+    for i in range(len(cu_q) - 1):
+        nq = int(cu_q[i + 1] - cu_q[i]); nk = int(cu_k[i + 1] - cu_k[i])
+        d0 = int(q_off[i]) - int(k_off[i])
+        for_rows = np.clip(d0 + 1 + np.arange(nq, dtype=np.int64), 0, nk)
+        total += int(for_rows.sum())
+    return total
+
+
+def cpu_baseline(w, g, budget_rows: int = 384):
+    """Time the fp64 oracle on a bounded row sample of the same share (CPU)."""
+    from oracle import share_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:   # pragma: no cover - threadpoolctl missing
+        threads = 1
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(int(g.cu_q[-1]), size=min(budget_rows, int(g.cu_q[-1])), replace=False))
+    seq = np.searchsorted(g.cu_q, rows, side="right") - 1
+    pairs = 0
+    for r, i in zip(rows, seq):
+        pos = int(g.q_off[i]) + int(r - g.cu_q[i])
+        pairs += min(pos + 1, int(g.cu_full[i + 1] - g.cu_full[i]))
+    t0 = time.perf_counter()
+    share_ref(g, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4 * w.d * w.hq * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(rows)} random query rows of the share x all {w.hq} heads against all "
+                      f"their visible keys (fp64 numpy, {dt:.1f} s, {flops / 1e9:.1f} GFLOP)",
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cp4_share")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; each rank's share is what one GPU computes.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as wl
+    import context_ring_attention_amd as cra
+
+    cra.load()
+    torch.cuda.set_device(0)
+    w = wl.make(args.workload, args.seed)
+    if len(w.groups) != 1 or w.dtype != "bf16":
+        print("bench.py times single-group bf16 share workloads", file=sys.stderr)
+        return 2
+    g = w.groups[0]
+    bf = torch.bfloat16
+    q = torch.from_numpy(g.q).to("cuda", bf)
+    ks = [torch.from_numpy(c.k).to("cuda", bf) for c in g.chunks]
+    vs = [torch.from_numpy(c.v).to("cuda", bf) for c in g.chunks]
+    cu_q = np.ascontiguousarray(g.cu_q, np.int32)
+    q_off = np.ascontiguousarray(g.q_off, np.int32)
+    cu_ks = [np.ascontiguousarray(c.cu_k, np.int32) for c in g.chunks]
+    k_offs = [np.ascontiguousarray(c.k_off, np.int32) for c in g.chunks]
+    bufs = cra.ShareBuffers.allocate(q, w.hkv, cu_q)
+    stream = torch.cuda.current_stream()
+
+    pairs_chunk = [visible_pairs(cu_q, c.cu_k, q_off, c.k_off) for c in g.chunks]
+    flops_chunk = [4 * w.d * w.hq * p for p in pairs_chunk]
+    flops_step = sum(flops_chunk)
+    tq = int(cu_q[-1])
+    merge_bytes = 3 * (tq * w.hq * w.d * 4 + tq * w.hq * 4)
+    n_merge = len(g.chunks) - 1
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    attn_ev = [[(ev(), ev()) for _ in g.chunks] for _ in range(args.steps)]
+    merge_ev = [[(ev(), ev()) for _ in range(n_merge)] for _ in range(args.steps)]
+
+    def step(i=None):
+        for c in range(len(g.chunks)):
+            out, lse = (bufs.o_acc, bufs.lse_acc) if c == 0 else (bufs.o_part, bufs.lse_part)
+            if i is not None:
+                attn_ev[i][c][0].record(stream)
+            cra.cpattn_fwd_chunk(q, ks[c], vs[c], cu_q, cu_ks[c], q_off, k_offs[c], True, out=out,
+                                 lse=lse, workspace=bufs.workspace, stream=stream)
+            if i is not None:
+                attn_ev[i][c][1].record(stream)
+            if c > 0:
+                if i is not None:
+                    merge_ev[i][c - 1][0].record(stream)
+                cra.cpattn_merge(bufs.o_acc, bufs.lse_acc, bufs.o_part, bufs.lse_part, stream=stream)
+                if i is not None:
+                    merge_ev[i][c - 1][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start, t_end = ev(), ev()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    value = flops_step / (ms_step / 1e3) / 1e12
+
+    attn_ms = sum(a.elapsed_time(b) for row in attn_ev for a, b in row)
+    merge_ms = sum(a.elapsed_time(b) for row in merge_ev for a, b in row)
+    n_attn = args.steps * len(g.chunks)
+    attn_avg_ms = attn_ms / n_attn
+    attn_flops_per_launch = flops_step / len(g.chunks)
+    attn_tflops = attn_flops_per_launch / (attn_avg_ms / 1e3) / 1e12
+    merge_avg_ms = merge_ms / max(1, args.steps * n_merge)
+    merge_gbs = merge_bytes / (merge_avg_ms / 1e3) / 1e9 if n_merge else None
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} (seed {w.seed}): last CP4 rank of a 16,384-token THD "
+                               f"pack, local Q {tq} tokens in {len(cu_q) - 1} sequences, "
+                               f"{len(g.chunks)} KV chunks of {int(cu_ks[0][-1])} tokens, "
+                               f"{w.hq}/{w.hkv} heads, D={w.d}, causal",
+                   "global_batch": 16384, "seq_len": int(max(w.lengths)), "parallelism": "cp4-share"},
+        "mfma_util": round(value / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "attn_fwd_bf16_kernel<128> (event-timed per cpattn_fwd_chunk call, "
+                               "plan upload included)",
+                     "avg_launch_us": round(attn_avg_ms * 1e3, 2),
+                     "flops_per_launch": attn_flops_per_launch},
+        "merge": {"avg_launch_us": round(merge_avg_ms * 1e3, 2) if n_merge else None,
+                  "bytes_per_launch": merge_bytes, "achieved_GBs": round(merge_gbs, 1) if merge_gbs else None,
+                  "hbm_frac": round(merge_gbs / HBM_PEAK_GBS, 4) if merge_gbs else None},
+        "flops_per_step": flops_step,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, g)
+        cb["value"] = float(f"{cb['value']:.4g}")
+        cb.pop("seconds", None)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,235 @@
+// C ABI of libcpattn: argument checks, plan upload, kernel dispatch.
+#include <algorithm>
+#include <cstring>
+#include <deque>
+#include <mutex>
+#include <vector>
+
+#include "internal.h"
+
+namespace cpattn {
+const char* last_error_text();
+void clear_error();
+
+namespace {
+
+// Plans are built on the host and copied into the caller's device workspace
+// with an asynchronous copy on the caller's stream.  The copy's source must
+// stay valid until the copy has run, so plans are staged in a pinned host ring
+// that the library owns (one per device, created on first use and kept for the
+// life of the process).  Before a region of the ring is reused, the event
+// recorded after the copy that last read it is waited on; in steady state
+// those copies finished long ago and the wait returns at once.
+class StagingRing {
+ public:
+  static constexpr size_t kCapacity = size_t(8) << 20;
+  static constexpr size_t kAlign = 256;
+
+  // Copy `bytes` produced by `fill` into device memory `dst` on `stream`.
+  template <class Fill>
+  cpattn_status upload(void* dst, size_t bytes, hipStream_t stream, Fill&& fill) {
+    std::lock_guard<std::mutex> lock(mu_);
+    if (!host_) {
+      if (hipHostMalloc(&host_, kCapacity, hipHostMallocDefault) != hipSuccess) {
+        host_ = nullptr;
+        return set_error(CPATTN_ERR_HIP, "hipHostMalloc of the plan staging ring failed");
+      }
+    }
+    if (bytes > kCapacity)
+      return set_error(CPATTN_ERR_UNSUPPORTED, "plan of %zu bytes exceeds the staging ring", bytes);
+    size_t begin = head_;
+    if (begin + bytes > kCapacity) begin = 0;
+    const size_t end = begin + bytes;
+    // Wait for every earlier copy that read [begin, end); drop finished fences.
+    for (auto it = fences_.begin(); it != fences_.end();) {
+      const bool overlap = it->begin < end && begin < it->end;
+      if (overlap) {
+        if (hipEventSynchronize(it->ev) != hipSuccess)
+          return set_error(CPATTN_ERR_HIP, "hipEventSynchronize on the staging ring failed");
+      }
+      if (overlap || hipEventQuery(it->ev) == hipSuccess) {
+        spare_.push_back(it->ev);
+        it = fences_.erase(it);
+      } else {
+        ++it;
+      }
+    }
+    char* src = static_cast<char*>(host_) + begin;
+    fill(src);
+    if (hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+      return set_error(CPATTN_ERR_HIP, "hipMemcpyAsync of the plan failed");
+    hipEvent_t ev;
+    if (!spare_.empty()) {
+      ev = spare_.back();
+      spare_.pop_back();
+    } else if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+      return set_error(CPATTN_ERR_HIP, "hipEventCreate failed");
+    }
+    if (hipEventRecord(ev, stream) != hipSuccess) {
+      spare_.push_back(ev);
+      return set_error(CPATTN_ERR_HIP, "hipEventRecord failed");
+    }
+    fences_.push_back(Fence{begin, end, ev});
+    head_ = (end + kAlign - 1) / kAlign * kAlign;
+    return CPATTN_OK;
+  }
+
+ private:
+  struct Fence {
+    size_t begin, end;
+    hipEvent_t ev;
+  };
+  std::mutex mu_;
+  void* host_ = nullptr;
+  size_t head_ = 0;
+  std::deque<Fence> fences_;
+  std::vector<hipEvent_t> spare_;
+};
+
+constexpr int kMaxDevices = 64;
+StagingRing g_rings[kMaxDevices];
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+}  // namespace
+}  // namespace cpattn
+
+using namespace cpattn;
+
+extern "C" {
+
+const char* cpattn_status_string(cpattn_status s) {
+  switch (s) {
+    case CPATTN_OK: return "ok";
+    case CPATTN_ERR_INVALID_ARG: return "invalid argument";
+    case CPATTN_ERR_UNSUPPORTED: return "unsupported";
+    case CPATTN_ERR_WORKSPACE: return "workspace too small";
+    case CPATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* cpattn_last_error(void) { return last_error_text(); }
+
+size_t cpattn_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q, int32_t hq, int32_t hkv,
+                             int32_t d) {
+  (void)d;
+  if (nseq < 0 || hq < 1 || hkv < 1 || (nseq > 0 && !cu_seqlens_q)) return 0;
+  for (int32_t i = 0; i < nseq; ++i)
+    if (cu_seqlens_q[i + 1] < cu_seqlens_q[i]) return 0;
+  // The smallest token block of any geometry (32 tokens) bounds the entry count.
+  const int64_t n = count_entries(cu_seqlens_q, nseq, kBf16RowsPerWave);
+  return std::max<size_t>(256, size_t(n) * sizeof(cpattn_plan_entry));
+}
+
+cpattn_status cpattn_plan_build(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
+                                cpattn_dtype dtype, int32_t causal, cpattn_plan_entry* plan,
+                                size_t plan_bytes, cpattn_plan_info* info) {
+  clear_error();
+  if (dtype != CPATTN_BF16 && dtype != CPATTN_FP32)
+    return set_error(CPATTN_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  cpattn_status st = validate_metadata(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset,
+                                       nseq, hq, hkv, d);
+  if (st != CPATTN_OK) return st;
+  const Geometry g = geometry_for(dtype, hq, hkv);
+  const int64_t n = count_entries(cu_seqlens_q, nseq, g.tokens_per_tile);
+  if (plan && plan_bytes < size_t(n) * sizeof(cpattn_plan_entry))
+    return set_error(CPATTN_ERR_WORKSPACE, "plan buffer of %zu bytes, need %zu", plan_bytes,
+                     size_t(n) * sizeof(cpattn_plan_entry));
+  build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq, causal, g, plan, n,
+                info);
+  if (info) {
+    info->head_groups = hq / g.heads_per_tile;
+    info->n_tiles = int32_t(n * info->head_groups);
+  }
+  return CPATTN_OK;
+}
+
+cpattn_status cpattn_fwd_chunk(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                               int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
+                               cpattn_dtype dtype, int32_t causal, float* o, float* lse,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  if (dtype != CPATTN_BF16 && dtype != CPATTN_FP32)
+    return set_error(CPATTN_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  cpattn_status st = validate_metadata(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset,
+                                       nseq, hq, hkv, d);
+  if (st != CPATTN_OK) return st;
+  const int64_t tq = cu_seqlens_q[nseq], tk = cu_seqlens_k[nseq];
+  if (tq == 0) return CPATTN_OK;  // nothing to write
+  const size_t esz = dtype == CPATTN_BF16 ? 2 : 4;
+  if (!q || !o || !lse) return set_error(CPATTN_ERR_INVALID_ARG, "q, o and lse must be non-null");
+  if (tk > 0 && (!k || !v)) return set_error(CPATTN_ERR_INVALID_ARG, "k and v must be non-null");
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4) || (tk > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+    return set_error(CPATTN_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned and lse 4-byte aligned");
+  const size_t q_bytes = size_t(tq) * hq * d * esz, kv_bytes = size_t(tk) * hkv * d * esz;
+  const size_t o_bytes = size_t(tq) * hq * d * 4, lse_bytes = size_t(tq) * hq * 4;
+  if (overlaps(o, o_bytes, q, q_bytes) || overlaps(o, o_bytes, k, kv_bytes) ||
+      overlaps(o, o_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, o, o_bytes))
+    return set_error(CPATTN_ERR_INVALID_ARG, "o/lse must not overlap q, k, v or each other");
+
+  const Geometry g = geometry_for(dtype, hq, hkv);
+  const int64_t n = count_entries(cu_seqlens_q, nseq, g.tokens_per_tile);
+  const size_t plan_bytes = size_t(n) * sizeof(cpattn_plan_entry);
+  if (!workspace || workspace_bytes < plan_bytes || !aligned(workspace, 256))
+    return set_error(CPATTN_ERR_WORKSPACE, "workspace of %zu bytes (need %zu, 256-byte aligned)",
+                     workspace_bytes, plan_bytes);
+  const int head_groups = hq / g.heads_per_tile;
+  if (n * head_groups > int64_t(INT32_MAX))
+    return set_error(CPATTN_ERR_UNSUPPORTED, "too many tiles for one launch");
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(CPATTN_ERR_HIP, "hipGetDevice failed");
+  st = g_rings[dev].upload(workspace, plan_bytes, stream, [&](char* dst) {
+    build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq, causal, g,
+                  reinterpret_cast<cpattn_plan_entry*>(dst), n, nullptr);
+  });
+  if (st != CPATTN_OK) return st;
+  const auto* plan = static_cast<const cpattn_plan_entry*>(workspace);
+  hipError_t err;
+  if (dtype == CPATTN_BF16) {
+    err = launch_attn_fwd_bf16(q, k, v, plan, int(n), head_groups, g.heads_per_tile, hq, hkv, d,
+                               int(tq), o, lse, stream);
+  } else {
+    err = launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                              static_cast<const float*>(v), plan, int(n), hq, hkv, d, int(tq), o,
+                              lse, stream);
+  }
+  if (err != hipSuccess)
+    return set_error(CPATTN_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
+  return CPATTN_OK;
+}
+
+cpattn_status cpattn_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,
+                           int64_t t, int32_t hq, int32_t d, hipStream_t stream) {
+  clear_error();
+  if (t < 0 || hq < 1 || d < 4 || d > 256 || (d & (d - 1)) != 0)
+    return set_error(CPATTN_ERR_INVALID_ARG, "merge needs t >= 0, hq >= 1, d a power of two in [4, 256]");
+  if (t == 0) return CPATTN_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b)
+    return set_error(CPATTN_ERR_INVALID_ARG, "merge buffers must be non-null");
+  if (!aligned(o_a, 16) || !aligned(o_b, 16) || !aligned(lse_a, 4) || !aligned(lse_b, 4))
+    return set_error(CPATTN_ERR_INVALID_ARG, "o must be 16-byte and lse 4-byte aligned");
+  const size_t ob = size_t(t) * hq * d * 4, lb = size_t(t) * hq * 4;
+  if (overlaps(o_a, ob, o_b, ob) || overlaps(o_a, ob, lse_b, lb) || overlaps(lse_a, lb, o_b, ob) ||
+      overlaps(lse_a, lb, lse_b, lb) || overlaps(o_a, ob, lse_a, lb))
+    return set_error(CPATTN_ERR_INVALID_ARG, "merge inputs must not overlap");
+  if (t * int64_t(hq) * (d / 4) > (int64_t(1) << 40))
+    return set_error(CPATTN_ERR_UNSUPPORTED, "merge too large");
+  hipError_t err = launch_merge(o_a, lse_a, o_b, lse_b, t, hq, d, stream);
+  if (err != hipSuccess)
+    return set_error(CPATTN_ERR_HIP, "merge launch failed: %s", hipGetErrorString(err));
+  return CPATTN_OK;
+}
+
+}  // extern "C"

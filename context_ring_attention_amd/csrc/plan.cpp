@@ -1,0 +1,142 @@
+// Host-side work planner: cu_seqlens + global position offsets -> ordered tiles.
+//
+// The causal mask is by global position (a query at q_pos sees keys with
+// k_pos <= q_pos of its own sequence), so under a KV chunk at offset k_off a
+// tile of query rows starting at q_off + row0 sees keys u <= delta + r with
+// delta = q_off + row0 - k_off.  The number of key blocks a tile visits is
+// therefore known on the host, and tiles are ordered longest first so that
+// the hardware's in-order work-group dispatch approximates longest-processing-
+// time scheduling of the causally unbalanced work (diagonal chunks give tiles
+// of 1..n blocks; sequences of a pack differ in length).
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace cpattn {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+cpattn_status set_error(cpattn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+const char* last_error_text() { return g_last_error.c_str(); }
+void clear_error() { g_last_error.clear(); }
+
+Geometry geometry_for(cpattn_dtype dtype, int hq, int hkv) {
+  if (dtype == CPATTN_FP32) return Geometry{kF32TokensPerTile, 1, kF32BlockN};
+  const int group = hq / hkv;
+  const int hpt = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+  return Geometry{kBf16RowsPerWave * kBf16Waves / hpt, hpt, kBf16BlockN};
+}
+
+cpattn_status validate_metadata(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_off,
+                                const int32_t* k_off, int32_t nseq, int32_t hq, int32_t hkv,
+                                int32_t d) {
+  if (nseq < 0) return set_error(CPATTN_ERR_INVALID_ARG, "nseq must be >= 0 (got %d)", nseq);
+  if (hq < 1 || hkv < 1) return set_error(CPATTN_ERR_INVALID_ARG, "hq and hkv must be >= 1");
+  if (hq % hkv != 0)
+    return set_error(CPATTN_ERR_INVALID_ARG, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
+  if (d != 64 && d != 128)
+    return set_error(CPATTN_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+  if (!cu_q || !cu_k)
+    return set_error(CPATTN_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be non-null");
+  if (cu_q[0] != 0 || cu_k[0] != 0)
+    return set_error(CPATTN_ERR_INVALID_ARG, "cu_seqlens must start at 0");
+  for (int32_t i = 0; i < nseq; ++i) {
+    if (cu_q[i + 1] < cu_q[i] || cu_k[i + 1] < cu_k[i])
+      return set_error(CPATTN_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (sequence %d)", i);
+    const int64_t qo = q_off ? q_off[i] : 0, ko = k_off ? k_off[i] : 0;
+    if (qo < 0 || ko < 0)
+      return set_error(CPATTN_ERR_INVALID_ARG, "position offsets must be >= 0 (sequence %d)", i);
+    if (qo + (cu_q[i + 1] - cu_q[i]) > INT32_MAX || ko + (cu_k[i + 1] - cu_k[i]) > INT32_MAX)
+      return set_error(CPATTN_ERR_INVALID_ARG, "positions of sequence %d overflow int32", i);
+  }
+  // Element indices are computed in 64-bit inside the kernels; rows stay int32.
+  return CPATTN_OK;
+}
+
+int64_t count_entries(const int32_t* cu_q, int32_t nseq, int tokens_per_tile) {
+  int64_t n = 0;
+  for (int32_t i = 0; i < nseq; ++i) {
+    const int64_t len = int64_t(cu_q[i + 1]) - cu_q[i];
+    n += (len + tokens_per_tile - 1) / tokens_per_tile;
+  }
+  return n;
+}
+
+// Visible pairs of one sequence: sum over query rows t of clamp(delta0 + t + 1, 0, nk).
+static int64_t visible_pairs(int64_t nq, int64_t nk, int64_t delta0, bool causal) {
+  if (!causal) return nq * nk;
+  int64_t total = 0;
+  // rows where the count grows linearly: delta0 + t + 1 in (0, nk)
+  const int64_t t_lo = std::max<int64_t>(0, -delta0);               // first row seeing >= 1 key
+  const int64_t t_full = std::max<int64_t>(0, nk - 1 - delta0);     // first row seeing all keys
+  const int64_t a = std::min(t_lo, nq), b = std::min(std::max(t_full, a), nq);
+  // rows a .. b-1 see delta0 + t + 1 keys
+  if (b > a) total += (b - a) * (delta0 + 1) + (b - 1 + a) * (b - a) / 2;
+  total += (nq - b) * nk;
+  return total;
+}
+
+void build_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_off,
+                   const int32_t* k_off, int32_t nseq, int32_t causal, const Geometry& g,
+                   cpattn_plan_entry* out, int64_t n, cpattn_plan_info* info) {
+  const int tt = g.tokens_per_tile, bn = g.block_n;
+  std::vector<cpattn_plan_entry> tmp;
+  cpattn_plan_entry* dst = out;
+  if (!dst && info) { tmp.resize(size_t(n)); dst = tmp.data(); }
+  int64_t e = 0, pairs = 0, blocks = 0;
+  for (int32_t i = 0; i < nseq; ++i) {
+    const int32_t nq = cu_q[i + 1] - cu_q[i], nk = cu_k[i + 1] - cu_k[i];
+    const int64_t qo = q_off ? q_off[i] : 0, ko = k_off ? k_off[i] : 0;
+    if (info) pairs += visible_pairs(nq, nk, qo - ko, causal != 0);
+    for (int32_t tb = 0; tb * int64_t(tt) < nq; ++tb) {
+      cpattn_plan_entry p;
+      p.row0 = cu_q[i] + tb * tt;
+      p.nrows = std::min<int32_t>(tt, nq - tb * tt);
+      p.k_start = cu_k[i];
+      p.k_len = nk;
+      int64_t delta = causal ? (qo + int64_t(tb) * tt - ko) : int64_t(nk);
+      delta = std::max<int64_t>(-tt, std::min<int64_t>(delta, nk));
+      p.delta = int32_t(delta);
+      const int64_t kend = std::max<int64_t>(0, std::min<int64_t>(nk, delta + p.nrows));
+      p.cost = int32_t((kend + bn - 1) / bn);
+      p.seq = i;
+      p.tblock = tb;
+      if (dst) dst[e] = p;
+      blocks += p.cost;
+      ++e;
+    }
+  }
+  if (dst) {
+    // Longest first; ties keep (sequence, token block) order so plans are deterministic.
+    std::stable_sort(dst, dst + n, [](const cpattn_plan_entry& a, const cpattn_plan_entry& b) {
+      return a.cost > b.cost;
+    });
+  }
+  if (info) {
+    info->n_entries = int32_t(n);
+    info->tokens_per_tile = tt;
+    info->heads_per_tile = g.heads_per_tile;
+    info->block_n = bn;
+    info->visible_pairs = pairs;
+    info->key_blocks = blocks;
+    info->plan_bytes = size_t(n) * sizeof(cpattn_plan_entry);
+  }
+}
+
+}  // namespace cpattn

@@ -1,0 +1,168 @@
+/*
+ * cpattn: chunked causal attention over packed variable-length sequences, and the
+ * log-sum-exp merge of partial results, on AMD Instinct MI355X (gfx950).
+ *
+ * This is the per-GPU compute of ring-style context parallelism as described in
+ * the "Megatron 6D parallelism guide", section 6 (context parallelism): each
+ * rank holds a slice S/CP of a sequence's queries, computes a flash-attention
+ * partial result against one KV chunk at a time, and folds each partial into a
+ * running result by the online-softmax update (running max m, running sum l,
+ * rescale factors alpha and beta), returning O / l at the end.  Inputs are
+ * "remove-padding / THD" packs (verl docs, "Dynamic Context Parallelism"): the
+ * sequences of a micro-batch are concatenated without padding and described by
+ * prefix sums of their lengths (cu_seqlens).
+ *
+ * Conventions shared by every call:
+ *   - THD tensors are row-major [T, H, D] with D fastest; element (t, h, d) is at
+ *     ((t * H) + h) * D + d.  They are contiguous and 16-byte aligned.
+ *   - LSE tensors are row-major [H, T] fp32, natural log.
+ *   - cu_seqlens arrays are int32 [nseq + 1], cu[0] == 0, non-decreasing; the
+ *     tensor holds cu[nseq] rows.  Sequence i owns rows cu[i] .. cu[i+1]-1.
+ *   - Query token t of sequence i has global position q_pos_offset[i] + t; key u
+ *     has k_pos_offset[i] + u.  With causal != 0 a query sees a key of the SAME
+ *     sequence iff key position <= query position (diagonal included).  Sequences
+ *     never see each other.  Without causal it sees every key of its sequence.
+ *   - Query head h reads kv head floor(h * hkv / hq) (contiguous GQA groups).
+ *   - Scores are scaled by 1/sqrt(d).
+ *   - A query with no visible key gets O = 0 and LSE = -inf (the empty partial:
+ *     the pages' initial state O = 0, m = -inf, l = 0, normalised).
+ *   - All device work is asynchronous on `stream`.  Device faults surface at the
+ *     caller's next synchronisation.  The library never aborts: invalid arguments
+ *     return a status code and leave every output untouched.
+ *   - Metadata arrays (cu_seqlens, offsets) live in HOST memory; all tensors live
+ *     in device memory of the current device.
+ */
+#ifndef CPATTN_H_
+#define CPATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CPATTN_OK = 0,
+  CPATTN_ERR_INVALID_ARG = 1,   /* malformed metadata, null or misaligned pointer, bad sizes */
+  CPATTN_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement (e.g. d not in {64,128}) */
+  CPATTN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than cpattn_workspace_size() */
+  CPATTN_ERR_HIP = 4            /* a HIP runtime call failed; see cpattn_last_error() */
+} cpattn_status;
+
+typedef enum {
+  CPATTN_BF16 = 0,              /* q, k, v are bfloat16; fp32 accumulation and softmax */
+  CPATTN_FP32 = 1               /* q, k, v are float32; fp32 throughout */
+} cpattn_dtype;
+
+/*
+ * Bytes of device workspace one cpattn_fwd_chunk call needs for these query
+ * sequences (the work plan).  cu_seqlens_q is host int32 [nseq + 1].  The value
+ * depends only on nseq, the query lengths and the head counts, so one workspace
+ * serves every KV chunk of a rank's share.  Returns 0 if the arguments are
+ * invalid (nseq < 0, null cu_seqlens_q with nseq > 0, hq or hkv < 1).
+ */
+size_t cpattn_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q, int32_t hq, int32_t hkv,
+                             int32_t d);
+
+/*
+ * One KV chunk: the flash-attention partial of the pages' ring loop
+ * ("Megatron 6D parallelism guide", section 6, the per-step call that returns
+ * O_step, m_step, l_step), returned in normalised form:
+ *     o   [Tq, hq, d] fp32 = O_step / l_step        (device, written)
+ *     lse [hq, Tq]    fp32 = m_step + ln l_step     (device, written)
+ * with Tq = cu_seqlens_q[nseq].
+ *
+ *   q       device [Tq, hq, d], dtype            (read)
+ *   k, v    device [Tk, hkv, d], dtype, Tk = cu_seqlens_k[nseq]  (read)
+ *   cu_seqlens_q, cu_seqlens_k   host int32 [nseq + 1]
+ *   q_pos_offset, k_pos_offset   host int32 [nseq], >= 0, or NULL for all zeros
+ *   hq % hkv == 0; d in {64, 128}
+ *   workspace        device, >= cpattn_workspace_size(...) bytes, 256-byte aligned;
+ *                    owned by the caller; it holds this call's work plan until the
+ *                    kernel has run, so consecutive calls on one stream may reuse it.
+ * The caller owns every buffer; o must not overlap q, k or v.  Rows of o/lse for
+ * queries of zero-length key sequences are written as (0, -inf).
+ * Returns CPATTN_OK, or an error code with nothing enqueued.
+ */
+cpattn_status cpattn_fwd_chunk(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                               int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
+                               cpattn_dtype dtype, int32_t causal, float* o, float* lse,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The online-softmax merge of the pages' ring loop ("Megatron 6D parallelism
+ * guide", section 6: m_new = max(m, m_step), alpha = exp(m - m_new),
+ * beta = exp(m_step - m_new), l = alpha*l + beta*l_step, O = alpha*O + beta*O_step),
+ * written for normalised partials over disjoint key sets.  In place:
+ *     (o_a, lse_a) <- merge((o_a, lse_a), (o_b, lse_b))
+ *   o_a, o_b     device fp32 [t, hq, d]
+ *   lse_a, lse_b device fp32 [hq, t]
+ *   d a power of two in [4, 256].
+ * An empty side (LSE = -inf) leaves the other side unchanged exactly; two empty
+ * sides stay (O_a, -inf).  The b buffers must not overlap the a buffers.
+ */
+cpattn_status cpattn_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,
+                           int64_t t, int32_t hq, int32_t d, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* cpattn_status_string(cpattn_status s);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char* cpattn_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Work plan (host only; exposed so the planner can be checked without a GPU).
+ *
+ * The kernels process "tiles": a run of consecutive query tokens of one
+ * sequence, for a group of query heads that share one kv head.  The planner
+ * turns host cu_seqlens and position offsets into one entry per (sequence,
+ * token block), orders the entries by descending cost (number of key blocks
+ * the tile must visit under the causal mask; longest first), and the launch
+ * walks them in that order, all head groups of an entry back to back.
+ *
+ * Plan layout: an array of cpattn_plan_entry (32 bytes each).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t row0;     /* first query row (index into Q's T dimension) of the tile */
+  int32_t nrows;    /* valid query tokens in the tile, 1 .. tokens_per_tile */
+  int32_t k_start;  /* first key row of the sequence in this chunk */
+  int32_t k_len;    /* keys of the sequence in this chunk */
+  int32_t delta;    /* tile row r sees key u iff u <= delta + r (clamped to [-tokens_per_tile, k_len]) */
+  int32_t cost;     /* key blocks the tile's last row must visit */
+  int32_t seq;      /* sequence index */
+  int32_t tblock;   /* token-block index within the sequence */
+} cpattn_plan_entry;
+
+typedef struct {
+  int32_t n_entries;        /* (sequence, token block) entries */
+  int32_t n_tiles;          /* work-groups launched = n_entries * head_groups */
+  int32_t tokens_per_tile;
+  int32_t heads_per_tile;
+  int32_t head_groups;      /* hq / heads_per_tile */
+  int32_t block_n;          /* keys per inner-loop block */
+  int64_t visible_pairs;    /* exact visible (query, key) pairs per query head */
+  int64_t key_blocks;       /* sum over entries of cost (key blocks visited per head group) */
+  size_t plan_bytes;        /* n_entries * sizeof(cpattn_plan_entry) */
+} cpattn_plan_info;
+
+/*
+ * Validate metadata and build the plan cpattn_fwd_chunk would launch.
+ * plan: host buffer of plan_bytes, or NULL to only fill *info.  Returns
+ * CPATTN_ERR_WORKSPACE if plan is non-NULL and plan_bytes is too small.
+ */
+cpattn_status cpattn_plan_build(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
+                                cpattn_dtype dtype, int32_t causal,
+                                cpattn_plan_entry* plan, size_t plan_bytes, cpattn_plan_info* info);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif  /* CPATTN_H_ */

@@ -1,0 +1,61 @@
+"""Helpers for the GPU parity tests: device copies and the tolerance checks."""
+import numpy as np
+
+# Output tolerance for bf16 inputs (fp32 accumulation) and for fp32 inputs.
+BF16_MAX_ABS, BF16_REL_L2 = 1e-2, 5e-3
+F32_MAX_ABS, F32_REL_L2 = 1e-5, 1e-5
+# LSE tolerance (the log-sum-exp is computed in fp32 from exact bf16 products).
+BF16_LSE_ABS, F32_LSE_ABS = 1e-3, 1e-5
+
+
+def dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device="cuda", dtype=getattr(torch, dtype)).contiguous()
+
+
+def dtype_name(w_dtype):
+    return "bfloat16" if w_dtype == "bf16" else "float32"
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
+    """Element-wise comparison: -inf pattern exact, O max-abs and rel-L2, LSE abs."""
+    o_gpu = np.asarray(o_gpu, np.float64); lse_gpu = np.asarray(lse_gpu, np.float64)
+    assert o_gpu.shape == o_ref.shape and lse_gpu.shape == lse_ref.shape, what
+    assert not np.isnan(o_gpu).any() and not np.isnan(lse_gpu).any(), f"NaN in output {what}"
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse_gpu), empty), f"-inf rows differ {what}"
+    assert np.all(o_gpu.transpose(1, 0, 2)[empty] == 0.0), f"empty rows not zero {what}"
+    max_abs, rel_l2, lse_tol = ((BF16_MAX_ABS, BF16_REL_L2, BF16_LSE_ABS) if dtype == "bf16"
+                                else (F32_MAX_ABS, F32_REL_L2, F32_LSE_ABS))
+    err = np.abs(o_gpu - o_ref)
+    worst = float(err.max()) if err.size else 0.0
+    nrm = float(np.linalg.norm(o_ref))
+    rel = float(np.linalg.norm(o_gpu - o_ref) / nrm) if nrm > 0 else 0.0
+    fin = ~empty
+    lse_err = float(np.abs(lse_gpu[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
+    assert worst <= max_abs, f"O max-abs {worst:.3e} > {max_abs} {what}"
+    assert rel <= rel_l2, f"O rel-L2 {rel:.3e} > {rel_l2} {what}"
+    assert lse_err <= lse_tol, f"LSE abs {lse_err:.3e} > {lse_tol} {what}"
+    return worst, rel, lse_err
+
+
+def sample_rows(cu_q, tokens_per_tile=32, extra=256, seed=0):
+    """Rows at every sequence's start/end, tile boundaries of each sequence, plus random rows."""
+    cu_q = np.asarray(cu_q, np.int64)
+    rows = set()
+    for i in range(len(cu_q) - 1):
+        a, b = int(cu_q[i]), int(cu_q[i + 1])
+        if b <= a:
+            continue
+        rows.update([a, min(a + 1, b - 1), b - 1, max(b - 2, a)])
+        for t in range(a, b, tokens_per_tile):
+            rows.update([t, min(t + tokens_per_tile - 1, b - 1)])
+    rng = np.random.default_rng(seed)
+    if cu_q[-1] > 0:
+        rows.update(rng.integers(0, int(cu_q[-1]), size=extra).tolist())
+    return np.array(sorted(rows), dtype=np.int64)

@@ -1,0 +1,182 @@
+"""Host side of libcpattn, on the CPU: exported symbols, the planner, error paths.
+
+No compute call reaches a GPU here: the planner is host code, and every
+invalid-argument path returns before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import visible_pairs_ref
+
+cra = pytest.importorskip("context_ring_attention_amd")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cra.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    with open(os.path.join(ROOT, "include", "cpattn.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(cpattn_\w+)\s*\(", text, re.M))
+    assert declared == set(cra.EXPORTED), declared ^ set(cra.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    # ...and that they are real dynamic symbols of the shared object
+    out = os.popen(f"nm -D --defined-only {cra.LIB_PATH}").read()
+    for name in declared:
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.cpattn_status_string(s)
+    assert b"unknown" in lib.cpattn_status_string(99)
+
+
+def _rows_of(entries):
+    return [(int(e["row0"]), int(e["nrows"])) for e in entries]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [(cra.BF16, 32, 8), (cra.BF16, 8, 1), (cra.BF16, 4, 4),
+                                          (cra.BF16, 6, 3), (cra.BF16, 4, 2), (cra.FP32, 2, 2)])
+def test_plan_covers_every_query_once_and_every_visible_key(dtype, hq, hkv):
+    rng = np.random.default_rng(hq * 7 + hkv)
+    for trial in range(25):
+        causal = trial % 5 != 0
+        nseq = int(rng.integers(0, 6))
+        q, k, v, cu_q, cu_k, qo, ko = wl.random_pack(rng, nseq, 300, 1, 1, 1, dtype="fp32")
+        entries, info = cra.cpattn_plan_build(cu_q, cu_k, qo, ko, hq=hq, hkv=hkv, d=128,
+                                              dtype=dtype, causal=causal)
+        tt, bn = info["tokens_per_tile"], info["block_n"]
+        assert hq % info["heads_per_tile"] == 0 and (hq // hkv) % info["heads_per_tile"] == 0
+        assert info["n_tiles"] == info["n_entries"] * hq // info["heads_per_tile"]
+        assert info["visible_pairs"] == visible_pairs_ref(cu_q, cu_k, qo, ko, causal)
+        # every query row appears in exactly one entry
+        cover = np.zeros(int(cu_q[-1]), dtype=int)
+        for e in entries:
+            assert 1 <= e["nrows"] <= tt
+            cover[e["row0"]:e["row0"] + e["nrows"]] += 1
+            i = int(e["seq"])
+            assert cu_q[i] <= e["row0"] and e["row0"] + e["nrows"] <= cu_q[i + 1]
+            assert e["row0"] == cu_q[i] + e["tblock"] * tt
+            assert e["k_start"] == cu_k[i] and e["k_len"] == cu_k[i + 1] - cu_k[i]
+            # the blocks visited cover every visible key of every row, and no more blocks
+            kpos = ko[i] + np.arange(e["k_len"])
+            last_visible = -1
+            for r in range(int(e["nrows"])):
+                t = e["row0"] - cu_q[i] + r
+                vis = (kpos <= qo[i] + t) if causal else np.ones_like(kpos, bool)
+                # the kernel's rule: row r sees u <= delta + r
+                rule = np.arange(e["k_len"]) <= e["delta"] + r
+                assert np.array_equal(vis, rule)
+                if vis.any():
+                    last_visible = max(last_visible, int(np.nonzero(vis)[0].max()))
+            assert e["cost"] == (last_visible + bn) // bn if last_visible >= 0 else e["cost"] == 0
+        assert np.all(cover == 1)
+        # longest first, ties in (sequence, block) order
+        costs = entries["cost"]
+        assert np.all(costs[:-1] >= costs[1:])
+        for a, b in zip(entries[:-1], entries[1:]):
+            if a["cost"] == b["cost"]:
+                assert (a["seq"], a["tblock"]) < (b["seq"], b["tblock"])
+
+
+def test_workspace_size_bounds_every_geometry():
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        nseq = int(rng.integers(0, 8))
+        cu = wl.cu_from_lengths(rng.integers(0, 500, size=nseq))
+        for dtype, hq, hkv in [(cra.BF16, 32, 8), (cra.BF16, 8, 8), (cra.FP32, 4, 2)]:
+            _, info = cra.cpattn_plan_build(cu, cu, None, None, hq=hq, hkv=hkv, d=64, dtype=dtype)
+            assert cra.cpattn_workspace_size(nseq, cu, hq, hkv, 64) >= info["plan_bytes"]
+
+
+def test_share_workload_plans():
+    """The 4,096-token CP4 share: diagonal chunk tiles cost 1..n blocks, the others n."""
+    pieces = wl.lengths_for("cp4_share", 0)
+    cu = wl.cu_from_lengths(pieces)
+    for c in range(4):
+        entries, info = cra.cpattn_plan_build(cu, cu, [3 * p for p in pieces], [c * p for p in pieces],
+                                              hq=32, hkv=8, d=128)
+        assert info["visible_pairs"] == visible_pairs_ref(cu, cu, [3 * p for p in pieces],
+                                                          [c * p for p in pieces])
+        if c < 3:
+            assert all(e["cost"] == -(-e["k_len"] // 64) for e in entries)
+        else:
+            assert entries["cost"].min() == 1
+
+
+# ----------------------------------------------------------------------------
+# error paths (all return a status, never abort, and touch no GPU)
+# ----------------------------------------------------------------------------
+BAD_PLANS = [
+    (dict(cu_q=[0, 5, 3], cu_k=[0, 5, 6]), cra._binding.ERR_INVALID_ARG),          # decreasing
+    (dict(cu_q=[1, 5], cu_k=[0, 5]), cra._binding.ERR_INVALID_ARG),                # does not start at 0
+    (dict(cu_q=[0, 5], cu_k=[0, 5], qo=[-1]), cra._binding.ERR_INVALID_ARG),       # negative offset
+    (dict(cu_q=[0, 5], cu_k=[0, 5], ko=[2**31 - 3]), cra._binding.ERR_INVALID_ARG),  # overflow
+    (dict(hq=6, hkv=4), cra._binding.ERR_INVALID_ARG),                            # hq % hkv
+    (dict(hq=0), cra._binding.ERR_INVALID_ARG),
+    (dict(d=96), cra._binding.ERR_UNSUPPORTED),
+    (dict(d=256), cra._binding.ERR_UNSUPPORTED),
+    (dict(dtype=7), cra._binding.ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_PLANS)
+def test_invalid_plan_arguments(kw, status):
+    args = dict(cu_q=[0, 5], cu_k=[0, 5], qo=None, ko=None, hq=4, hkv=2, d=64, dtype=cra.BF16)
+    args.update(kw)
+    with pytest.raises(cra.CpattnError) as ei:
+        cra.cpattn_plan_build(args["cu_q"], args["cu_k"], args["qo"], args["ko"], hq=args["hq"],
+                              hkv=args["hkv"], d=args["d"], dtype=args["dtype"])
+    assert ei.value.status == status
+
+
+def _i32(a):
+    arr = np.ascontiguousarray(a, dtype=np.int32)
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def test_fwd_chunk_rejects_bad_arguments_without_a_gpu(lib):
+    cu, pcu = _i32([0, 64])
+    fake = ctypes.c_void_p(4096)          # never dereferenced: validation fails first
+    mis = ctypes.c_void_p(4096 + 8)       # not 16-byte aligned
+    ws = ctypes.c_void_p(1 << 20)
+    call = lambda **kw: lib.cpattn_fwd_chunk(
+        kw.get("q", fake), kw.get("k", fake), kw.get("v", fake), kw.get("cuq", pcu),
+        kw.get("cuk", pcu), None, None, kw.get("nseq", 1), kw.get("hq", 4), kw.get("hkv", 2),
+        kw.get("d", 64), kw.get("dtype", 0), 1, kw.get("o", ctypes.c_void_p(1 << 30)),
+        kw.get("lse", ctypes.c_void_p(1 << 31)), kw.get("ws", ws), kw.get("wsb", 1 << 20), None)
+    assert call(q=ctypes.c_void_p(0)) == cra._binding.ERR_INVALID_ARG
+    assert call(q=mis) == cra._binding.ERR_INVALID_ARG
+    assert call(d=80) == cra._binding.ERR_UNSUPPORTED
+    assert call(hq=3) == cra._binding.ERR_INVALID_ARG
+    assert call(dtype=5) == cra._binding.ERR_INVALID_ARG
+    assert call(nseq=-1) == cra._binding.ERR_INVALID_ARG
+    assert call(ws=ctypes.c_void_p(0)) == cra._binding.ERR_WORKSPACE
+    assert call(wsb=8) == cra._binding.ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == cra._binding.ERR_WORKSPACE   # misaligned
+    assert call(o=ctypes.c_void_p(4096)) == cra._binding.ERR_INVALID_ARG            # o aliases q
+    bad, pbad = _i32([0, 70, 64])
+    assert call(cuq=pbad, nseq=2) == cra._binding.ERR_INVALID_ARG
+    assert b"non-decreasing" in lib.cpattn_last_error()
+    empty, pempty = _i32([0])
+    assert call(cuq=pempty, cuk=pempty, nseq=0) == cra._binding.OK                # nothing to do
+
+
+def test_merge_rejects_bad_arguments_without_a_gpu(lib):
+    a, b = ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 32)
+    la, lb = ctypes.c_void_p(1 << 33), ctypes.c_void_p(1 << 34)
+    assert lib.cpattn_merge(a, la, b, lb, 16, 2, 96, None) == cra._binding.ERR_INVALID_ARG
+    assert lib.cpattn_merge(a, la, b, lb, -1, 2, 64, None) == cra._binding.ERR_INVALID_ARG
+    assert lib.cpattn_merge(a, la, a, lb, 16, 2, 64, None) == cra._binding.ERR_INVALID_ARG   # alias
+    assert lib.cpattn_merge(None, la, b, lb, 16, 2, 64, None) == cra._binding.ERR_INVALID_ARG
+    assert lib.cpattn_merge(a, la, b, lb, 0, 2, 64, None) == cra._binding.OK              # empty
