@@ -39,8 +39,8 @@ def visible_pairs(cu_q, cu_k, q_off, k_off) -> int:
     return total
 
 
-def cpu_baseline(w, g, budget_rows: int = 384):
-    """Time the fp64 oracle on a bounded row sample of the same share (CPU)."""
+def cpu_baseline(w, g, budget_rows: int = 4096):
+    """Time the fp64 oracle on (a bounded row sample of) the same share, on the host CPU."""
     from oracle import share_ref
     try:
         from threadpoolctl import threadpool_info
@@ -72,6 +72,9 @@ def main() -> int:
     ap.add_argument("--workload", default="cp4_share")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run one plain elementwise copy of MIB MiB "
+                         "(reference point for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}): this build has no "
@@ -181,6 +184,13 @@ def main() -> int:
         "flops_per_step": flops_step,
         "cpu_baseline": None,
     }
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": n * 4, "written": n * 4}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, g)
         cb["value"] = float(f"{cb['value']:.4g}")

@@ -47,6 +47,8 @@ def build(verbose: bool = False) -> str:
         outs = list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"
     outs.append(_run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]))
+    import ctypes
+    ctypes.CDLL(tmp)          # fail the build if any symbol is left undefined
     os.replace(tmp, LIB)
     if verbose:
         for o in outs:

@@ -15,16 +15,27 @@
 // l and lane l^32 together hold all 32 keys of that token.  Row statistics thus
 // need one cross-half swap (v_permlane32_swap) per key block and no LDS.  The
 // output is accumulated transposed too, O^T[d][token] = V^T * P^T: P comes
-// straight from the score registers (bf16-rounded) as the B operand and V^T is
-// the A operand read from LDS.  Both operands of each MFMA use the same
-// (lane-group, element) -> k index mapping, so the contraction pairs the right
-// keys whatever order the hardware sums them in.
+// straight from the score registers (bf16-rounded) as the B operand, and V^T
+// is the A operand, gathered from row-major V in LDS by the gfx950 transpose
+// read (ds_read_b64_tr_b16 hands each lane 4 consecutive keys of its own d
+// column).  Both operands of each MFMA use the same (lane-group, element) -> k
+// index mapping, so the contraction pairs the right keys.
 //
-// LDS per stage: K [64][D] bf16 (row-major, 16-byte chunks XOR-swizzled by row)
-// and V^T [D][64] bf16 (keys permuted inside each group of 16 so that one lane's
-// eight P keys are contiguous; chunks XOR-swizzled by row).  Two stages: block
-// j+1 is fetched from HBM into registers while block j is computed, then stored
-// to the other stage; one barrier per block.
+// Data movement: K and V blocks go from HBM straight into LDS
+// (buffer_load_dwordx4 ... lds, 16 bytes per lane), through buffer resources
+// whose range ends at the sequence's last key, so rows past the end read as
+// zero with no branches.  16-byte chunks are XOR-swizzled by row (one pattern
+// for the K reads, another for the V transpose reads) against bank conflicts;
+// the swizzle is applied by choosing which global chunk each lane fetches.  Two
+// LDS stages: block j+1 is in flight while block j is computed; one barrier per
+// block.
+//
+// Softmax: scores stay in raw units s = q.k; p = exp2(s * c - m * c) with
+// c = log2(e)/sqrt(D).  The running max m is only moved when a row's block max
+// exceeds it by more than 8/c (a factor 2^8 in p): until then p <= 2^8, which
+// fp32 sums and bf16 P carry without loss of relative precision, and the final
+// O / l cancels the common factor exactly.  This skips the 64-register rescale
+// of the accumulator on almost every block.
 //
 // Masking: the host classifies blocks by global position, so only blocks on the
 // causal diagonal or past the sequence end pay for per-element masking.  A row
@@ -35,30 +46,38 @@ namespace cpattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kThreads = kBf16Waves * 64;
-constexpr int BN = kBf16BlockN;  // keys per block
+constexpr int BN = kBf16BlockN;          // keys per block
+constexpr float kRescaleLog2 = 8.0f;     // move the running max only past 2^8 growth
+constexpr int kBufferWord3 = 0x00020000; // raw buffer, 32-bit data format
 
 template <int D>
 struct Layout {
-  static constexpr int kChunks = D / 8;                 // 16-byte chunks per K row
-  static constexpr int kKBytes = BN * D * 2;
-  static constexpr int kVBytes = D * BN * 2;
-  static constexpr int kStage = kKBytes + kVBytes;
-  static constexpr int kKLoads = BN * kChunks / kThreads;  // 16-byte K loads per thread
-  static constexpr int kVTiles = (BN / 4) * kChunks;       // 4-key x 8-d tiles of V
+  static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = BN * kRowBytes;     // one K or V block
+  static constexpr int kStage = 2 * kTileBytes;         // K block then V block
+  static constexpr int kRowsPerKB = 1024 / kRowBytes;   // rows one wave-wide load fills
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kBf16Waves;
 
-  // byte offset of K (row r, chunk c) inside a stage
-  __device__ static __forceinline__ int k_off(int r, int c) {
-    const int sw = (D == 128) ? (r & 15) : ((r >> 1) & 7);
-    return r * (D * 2) + ((c ^ sw) << 4);
+  // K is read 16 bytes per lane along a column of 32 rows: spread rows over chunks.
+  __device__ static __forceinline__ int k_swz(int row) {
+    return (D == 128) ? (row & 15) : ((row >> 1) & 7);
   }
-  // byte offset of V^T (row d, 16-byte chunk c of 8 key positions) inside a stage
-  __device__ static __forceinline__ int vt_off(int d, int c) {
-    return kKBytes + d * (BN * 2) + ((c ^ ((d >> 1) & 7)) << 4);
+  // V is read by 16-lane groups, 4 rows x 32 bytes each: spread the 4 rows.
+  __device__ static __forceinline__ int v_swz(int row) {
+    return (D == 128) ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+  }
+  __device__ static __forceinline__ int k_off(int row, int c) {
+    return row * kRowBytes + ((c ^ k_swz(row)) << 4);
+  }
+  __device__ static __forceinline__ int v_off(int row, int c) {
+    return kTileBytes + row * kRowBytes + ((c ^ v_swz(row)) << 4);
   }
 };
 
@@ -68,7 +87,7 @@ struct Layout {
 __device__ __forceinline__ float pair_max(float x) {
   const unsigned u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_max(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float pair_sum(float x) {
@@ -77,19 +96,33 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// Buffer resources are a device-only type: the host pass of this file only
+// needs the kernel's launch stub, so device helpers and the kernel body are
+// compiled in the device pass alone.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const __bf16* base, int64_t rows_left,
+                                                           int64_t stride_bytes, int row_bytes) {
+  // Bytes from `base` to the end of the last valid row (0 if none).
+  const int64_t n = rows_left > 0 ? (rows_left - 1) * stride_bytes + row_bytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(base), (short)0,
+                                           int(n > 0x7fffffff ? 0x7fffffff : n), kBufferWord3);
+}
+#endif
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const cpattn_plan_entry* __restrict__ plan, int head_groups, int heads_per_tile, int hq,
     int hkv, int tq_total, float scale, float scale_log2, float* __restrict__ o,
     float* __restrict__ lse) {
+#if defined(__HIP_DEVICE_COMPILE__)
   using L = Layout<D>;
   constexpr int KS = D / 16;  // k-steps of the score MFMA
   constexpr int DT = D / 32;  // 32-row tiles of O^T
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * L::kStage];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31;  // token column of the MFMA tiles
   const int g = lane >> 5;  // lane half
@@ -100,7 +133,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const cpattn_plan_entry pe = plan[e];
   const int head = hg * heads_per_tile + (wave % heads_per_tile);
   const int tok0 = (wave / heads_per_tile) * kBf16RowsPerWave;
-  const int kvh = head / (hq / hkv);
+  const int kvh = (hg * heads_per_tile) / (hq / hkv);  // shared by every head of the tile
 
   // Per-wave key range (rows tok0 .. tok0 + rows_w - 1 of the tile).
   const int rows_w = min(max(pe.nrows - tok0, 0), kBf16RowsPerWave);
@@ -118,120 +151,96 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const bool ok = n < rows_w;
     const __bf16* qp = q + (int64_t(pe.row0 + tok0 + n) * hq + head) * D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ok) {
-        qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
-      } else {
-        qf[ks] = bf16x8{};
-      }
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * ks) : bf16x8{};
   }
 
   f32x16 acc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;  // running max of raw scores (row n)
+  float m_run = -INFINITY;  // running reference max of raw scores (row n)
   float l_run = 0.f;        // running sum over this lane's keys
+  const float thr = kRescaleLog2 / scale_log2;
 
-  // Global -> register staging of one K/V block.
-  u32x4 kreg[L::kKLoads];
-  u32x4 vreg[4];
-  const int kc = tid % L::kChunks;
-  const int kr = tid / L::kChunks;
-  constexpr int kRowStep = kThreads / L::kChunks;
-  const bool v_owner = tid < L::kVTiles;
-  const int vdg = tid % L::kChunks;  // d chunk of the V tile
-  const int vkg = tid / L::kChunks;  // 4-key group of the V tile
-  const int64_t kv_stride = int64_t(hkv) * D;
+  // ---- HBM -> LDS block loads (each wave fills kLoadsPerWave KB of K and of V) ----
+  const int64_t stride_bytes = int64_t(hkv) * D * 2;
   const __bf16* kbase = k + (int64_t(pe.k_start) * hkv + kvh) * D;
   const __bf16* vbase = v + (int64_t(pe.k_start) * hkv + kvh) * D;
-
-  auto fetch = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < L::kKLoads; ++i) {
-      const int key = j * BN + kr + i * kRowStep;
-      if (key < pe.k_len) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + key * kv_stride + 8 * kc);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    if (v_owner) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = j * BN + 4 * vkg + i;
-        if (key < pe.k_len) {
-          vreg[i] = *reinterpret_cast<const u32x4*>(vbase + key * kv_stride + 8 * vdg);
-        } else {
-          vreg[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  };
-
-  auto stash = [&](int stage) {
+  auto issue = [&](int j, int stage) {
+    const int64_t rows_left = int64_t(pe.k_len) - int64_t(j) * BN;
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kbase + int64_t(j) * BN * hkv * D, rows_left,
+                                                stride_bytes, D * 2);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vbase + int64_t(j) * BN * hkv * D, rows_left,
+                                                stride_bytes, D * 2);
     char* s = smem + stage * L::kStage;
 #pragma unroll
-    for (int i = 0; i < L::kKLoads; ++i)
-      *reinterpret_cast<u32x4*>(s + L::k_off(kr + i * kRowStep, kc)) = kreg[i];
-    if (v_owner) {
-      // keys 4*vkg .. +3 land at positions swap(bits 2,3) inside their 16-group
-      const int pos = 16 * (vkg >> 2) + 8 * (vkg & 1) + 4 * ((vkg >> 1) & 1);
-      const int pc = pos >> 3, pb = (pos & 7) * 2;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // d = 8 vdg + 2w (low halves) and 8 vdg + 2w + 1 (high halves)
-        const unsigned a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
-        u32x2 lo, hi;
-        lo[0] = (a0 & 0xFFFFu) | (a1 << 16);
-        lo[1] = (a2 & 0xFFFFu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
-        const int d0 = 8 * vdg + 2 * w;
-        *reinterpret_cast<u32x2*>(s + L::vt_off(d0, pc) + pb) = lo;
-        *reinterpret_cast<u32x2*>(s + L::vt_off(d0 + 1, pc) + pb) = hi;
-      }
+    for (int i = 0; i < L::kLoadsPerWave; ++i) {
+      // this wave fills the i-th of its 1 KB pieces; lane l fills bytes [16 l, 16 l + 16)
+      const int blk = wave * L::kLoadsPerWave + i;
+      const int row = blk * L::kRowsPerKB + lane / L::kChunks;
+      const int pc = lane % L::kChunks;                  // physical chunk this lane fills
+      const int voff = row * int(stride_bytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(s + blk * 1024), 16,
+                                               voff + ((pc ^ L::k_swz(row)) << 4), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(s + L::kTileBytes + blk * 1024), 16,
+                                               voff + ((pc ^ L::v_swz(row)) << 4), 0, 0, 0);
     }
   };
 
-  if (nblk > 0) fetch(0);
+  // Lane-constant parts of the LDS read addresses.
+  int k_rd[2][KS];  // S^T A operand: K row 32 kt + n, chunk 2 ks + g
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_rd[kt][ks] = L::k_off(32 * kt + n, 2 * ks + g);
+  // O^T A operand via transpose reads: lane (n, g) in 16-lane group (g, h = n / 16) supplies the
+  // address of V row 16 kk + 4 g + jr (+ 8 for the second half) at columns 32 dt + 16 h + 4 q.
+  const int jr = (n & 15) >> 2, qq = n & 3, hh = n >> 4;
+
+  if (nblk > 0) issue(0, 0);
 
   for (int j = 0; j < nblk; ++j) {
     const int stage = j & 1;
-    stash(stage);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 1 < nblk) fetch(j + 1);
+    if (j + 1 < nblk) issue(j + 1, stage ^ 1);
     if (j < nblk_w) {
       const char* s = smem + stage * L::kStage;
       // ---- S^T = K Q^T for 64 keys (two 32-key tiles) ----
       f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(s + L::k_off(n, 2 * ks + g));
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(s + L::k_off(32 + n, 2 * ks + g));
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][ks]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][ks]);
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
       }
       // ---- mask (diagonal / ragged blocks only) ----
       if (j >= nfull_w) {
         // key (within block) of register r: 32 kt + 8 (r / 4) + 4 g + r % 4
-        const int lim = min(pe.k_len - 1, pe.delta + tok0 + n) - j * BN;
+        const int lim = min(pe.k_len - 1, pe.delta + tok0 + n) - j * BN - 4 * g;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kin = 8 * (r >> 2) + 4 * g + (r & 3);
+          const int kin = 8 * (r >> 2) + (r & 3);
           if (kin > lim) s0[r] = -INFINITY;
           if (32 + kin > lim) s1[r] = -INFINITY;
         }
       }
       // ---- online softmax ----
-      float mx = -INFINITY;
+      float mx = __builtin_elementwise_max(s0[0], s1[0]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(s0[r], s1[r]));
       mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
-      const float neg = -m_use * scale_log2;
+      if (__any(mx > m_run + thr)) {
+        const float m_new = __builtin_elementwise_max(m_run, mx);
+        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * scale_log2);
+#pragma unroll
+        for (int i = 0; i < DT; ++i) acc[i] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * scale_log2;
       float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -239,12 +248,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, neg));
         psum += s0[r] + s1[r];
       }
-      l_run = l_run * alpha + psum;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int i = 0; i < DT; ++i) acc[i] *= alpha;
-      }
-      m_run = m_new;
+      l_run += psum;
       // P as bf16 B operands: key group kk takes registers 8 (kk % 2) .. +7 of tile kk / 2
       bf16x8 pf[4];
 #pragma unroll
@@ -256,10 +260,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       }
       // ---- O^T += V^T P^T ----
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int kk = 0; kk < 4; ++kk) {
+        const int row = 16 * kk + 4 * g + jr;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(s + L::vt_off(32 * dt + n, 2 * kk + g));
+        for (int dt = 0; dt < DT; ++dt) {
+          const int c16 = 4 * dt + 2 * hh + (qq >> 1);
+          const int off0 = L::v_off(row, c16) + 8 * (qq & 1);
+          const int off1 = L::v_off(row + 8, c16) + 8 * (qq & 1);
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off0));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off1));
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], acc[dt], 0, 0, 0);
         }
       }
@@ -285,6 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       lse[int64_t(head) * tq_total + row] = l_tot > 0.f ? m_run * scale + logf(l_tot) : -INFINITY;
     }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 }  // namespace
