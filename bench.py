@@ -185,11 +185,17 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if args.copy_calibration:
+        # A plain elementwise copy of known size whose source is not cache-resident:
+        # fill the source, stream 2 GiB through the caches, then copy.
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
+        evict = torch.empty(2 << 28, dtype=torch.float32, device="cuda")
+        evict.fill_(2.0)
+        torch.cuda.synchronize()
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
+        del evict
         result["copy_calibration_bytes"] = {"read": n * 4, "written": n * 4}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, g)

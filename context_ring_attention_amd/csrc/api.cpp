@@ -122,8 +122,8 @@ size_t cpattn_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q, int32_t 
   if (nseq < 0 || hq < 1 || hkv < 1 || (nseq > 0 && !cu_seqlens_q)) return 0;
   for (int32_t i = 0; i < nseq; ++i)
     if (cu_seqlens_q[i + 1] < cu_seqlens_q[i]) return 0;
-  // The smallest token block of any geometry (32 tokens) bounds the entry count.
-  const int64_t n = count_entries(cu_seqlens_q, nseq, kBf16RowsPerWave);
+  // The smallest token block of any geometry bounds the entry count.
+  const int64_t n = count_entries(cu_seqlens_q, nseq, kMinTileTokens);
   return std::max<size_t>(256, size_t(n) * sizeof(cpattn_plan_entry));
 }
 

@@ -37,9 +37,17 @@
 // O / l cancels the common factor exactly.  This skips the 64-register rescale
 // of the accumulator on almost every block.
 //
+// Row sums are taken on the bf16-rounded P with v_dot2_f32_bf16 (two keys per
+// instruction), so l sums exactly the weights the PV product multiplies.
+//
 // Masking: the host classifies blocks by global position, so only blocks on the
 // causal diagonal or past the sequence end pay for per-element masking.  A row
 // with no visible key keeps m = -inf and l = 0 and is written as (0, -inf).
+//
+// This file is compiled with -fno-honor-nans: no value here is ever NaN (scores
+// are finite or -inf, exp2(-inf) = 0), and without the flag every max over an
+// MFMA result is preceded by a canonicalising v_max_f32 x, x.  Infinities keep
+// their IEEE meaning.
 #include "internal.h"
 
 namespace cpattn {
@@ -47,6 +55,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -207,13 +216,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     if (j < nblk_w) {
       const char* s = smem + stage * L::kStage;
       // ---- S^T = K Q^T for 64 keys (two 32-key tiles) ----
+      // K fragments are read one k-step ahead of the MFMAs that consume them.
       f32x16 s0 = f32x16{}, s1 = f32x16{};
+      bf16x8 a0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][0]);
+      bf16x8 a1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][0]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][ks]);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][ks]);
+        bf16x8 n0, n1;
+        if (ks + 1 < KS) {
+          n0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][ks + 1]);
+          n1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][ks + 1]);
+        }
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+        if (ks + 1 < KS) {
+          a0 = n0;
+          a1 = n1;
+        }
       }
       // ---- mask (diagonal / ragged blocks only) ----
       if (j >= nfull_w) {
@@ -227,10 +246,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         }
       }
       // ---- online softmax ----
-      float mx = __builtin_elementwise_max(s0[0], s1[0]);
+      float mx;
+      {
+        float t[16];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(s0[r], s1[r]));
-      mx = pair_max(mx);
+        for (int r = 0; r < 16; ++r) t[r] = __builtin_elementwise_max(s0[r], s1[r]);
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+          for (int r = 0; r < w; ++r) t[r] = __builtin_elementwise_max(t[r], t[r + w]);
+        mx = pair_max(t[0]);
+      }
       if (__any(mx > m_run + thr)) {
         const float m_new = __builtin_elementwise_max(m_run, mx);
         const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
@@ -241,14 +267,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         m_run = m_new;
       }
       const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * scale_log2;
-      float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, neg));
         s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, neg));
-        psum += s0[r] + s1[r];
       }
-      l_run += psum;
       // P as bf16 B operands: key group kk takes registers 8 (kk % 2) .. +7 of tile kk / 2
       bf16x8 pf[4];
 #pragma unroll
@@ -257,6 +280,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         pf[1][jj] = (__bf16)s0[8 + jj];
         pf[2][jj] = (__bf16)s1[jj];
         pf[3][jj] = (__bf16)s1[8 + jj];
+      }
+      {
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float part[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          part[kk] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            part[kk] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[kk][2 * i], pf[kk][2 * i + 1]},
+                                                       ones, part[kk], false);
+        }
+        l_run += (part[0] + part[1]) + (part[2] + part[3]);
       }
       // ---- O^T += V^T P^T ----
 #pragma unroll

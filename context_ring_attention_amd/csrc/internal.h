@@ -10,15 +10,17 @@
 
 namespace cpattn {
 
-// Tile geometry of each kernel.  The bf16 kernel runs 4 waves per work-group,
-// each wave owning 32 query tokens of one head; heads_per_tile waves share a
-// token block, so a tile covers 32 * 4 / heads_per_tile tokens.  The fp32
-// kernel runs one head and 64 tokens per work-group.
+// Tile geometry of each kernel.  The bf16 kernel runs 4 waves per work-group
+// (one per SIMD), each wave owning 64 query tokens of one head; heads_per_tile
+// waves share a token block, so a tile covers 64 * 4 / heads_per_tile tokens.
+// The fp32 kernel runs one head and 64 tokens per work-group.
 constexpr int kBf16Waves = 4;
 constexpr int kBf16RowsPerWave = 32;
 constexpr int kBf16BlockN = 64;
 constexpr int kF32TokensPerTile = 64;
 constexpr int kF32BlockN = 32;
+// Smallest token block of any geometry (bounds the number of plan entries).
+constexpr int kMinTileTokens = kBf16RowsPerWave < kF32TokensPerTile ? kBf16RowsPerWave : kF32TokensPerTile;
 
 struct Geometry {
   int tokens_per_tile;

@@ -4,8 +4,11 @@ import numpy as np
 # Output tolerance for bf16 inputs (fp32 accumulation) and for fp32 inputs.
 BF16_MAX_ABS, BF16_REL_L2 = 1e-2, 5e-3
 F32_MAX_ABS, F32_REL_L2 = 1e-5, 1e-5
-# LSE tolerance (the log-sum-exp is computed in fp32 from exact bf16 products).
-BF16_LSE_ABS, F32_LSE_ABS = 1e-3, 1e-5
+# LSE tolerance.  The bf16 kernel sums l over the bf16-rounded probabilities the PV
+# product multiplies; each carries at most 2^-8 relative rounding (round to nearest
+# even, 8 significant bits), so |dLSE| <= ln(1 + 2^-8) = 3.9e-3 plus fp32 terms.
+# The fp32 kernel keeps every quantity in fp32.
+BF16_LSE_ABS, F32_LSE_ABS = 4e-3, 1e-5
 
 
 def dev(x, dtype):
