@@ -26,6 +26,13 @@ sys.path.insert(0, HERE)
 METRIC = "causal attn TFLOP/s + MFMA util%, 16K-token THD pack at CP4-share, 1 GPU"
 BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+ATTN_SOURCE = os.path.join(HERE, "context_ring_attention_amd", "csrc", "attn_fwd_bf16.hip")
+# HBM bytes per attention launch on this workload, from rocprofv3 FETCH_SIZE and WRITE_SIZE
+# runs (scaled by a plain-copy calibration), keyed by the sha256 of the kernel source they
+# were taken on.  Any other source reports traffic as null until it is profiled again.
+PROFILED_TRAFFIC = {
+    "39c909d6413ed85e8132368b88218206724352465a99ffbfe784ecd66b444c8b": 132298236,
+}
 
 
 def visible_pairs(cu_q, cu_k, q_off, k_off) -> int:
@@ -152,6 +159,11 @@ def main() -> int:
     merge_avg_ms = merge_ms / max(1, args.steps * n_merge)
     merge_gbs = merge_bytes / (merge_avg_ms / 1e3) / 1e9 if n_merge else None
 
+    import hashlib
+    with open(ATTN_SOURCE, "rb") as f:
+        traffic = PROFILED_TRAFFIC.get(hashlib.sha256(f.read()).hexdigest())
+    tk = int(cu_ks[0][-1])
+    attn_bytes = tq * w.hq * w.d * 2 + 2 * tk * w.hkv * w.d * 2 + tq * w.hq * w.d * 4 + tq * w.hq * 4
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -173,7 +185,9 @@ def main() -> int:
         "mfma_util": round(value / BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)",
+                     "algorithmic_bytes_per_launch": attn_bytes,
                      "kernel": "attn_fwd_bf16_kernel<128> (event-timed per cpattn_fwd_chunk call, "
                                "plan upload included)",
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
