@@ -2,17 +2,21 @@
 """Benchmark: one CP4 rank's share of a 16,384-token packed budget on one MI355X.
 
 A step is one pass of the whole per-rank hot path on the share's inputs (already
-resident in HBM): for each of the 4 KV chunks, host planning + plan upload +
-the attention kernel (cpattn_fwd_chunk), and after each chunk but the first the
-LSE merge (cpattn_merge) into the running result.  `value` is the share's
-algorithmic causal FLOPs (4 * D * Hq per visible query/key pair) divided by the
-step time.  Prints ONE JSON line.
+resident in HBM): host planning, plan upload and ONE cpattn_fwd_chunks launch that
+walks every KV chunk of the share with the online softmax carried across chunks
+(the ring loop's merges done in registers).  `value` is the share's algorithmic
+causal FLOPs (4 * D * Hq per visible query/key pair) divided by the step time.
+The two other schedules of the same share -- per-chunk launches accumulating in
+the epilogue (cpattn_fwd_chunk_accum), and per-chunk partials merged by
+cpattn_merge -- are timed the same way and reported under "schedules".
+Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload cp4_share] [--seed 0]
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -107,7 +111,8 @@ def main() -> int:
     q_off = np.ascontiguousarray(g.q_off, np.int32)
     cu_ks = [np.ascontiguousarray(c.cu_k, np.int32) for c in g.chunks]
     k_offs = [np.ascontiguousarray(c.k_off, np.int32) for c in g.chunks]
-    bufs = cra.ShareBuffers.allocate(q, w.hkv, cu_q)
+    nch = len(g.chunks)
+    bufs = cra.ShareBuffers.allocate(q, w.hkv, cu_q, nch)
     stream = torch.cuda.current_stream()
 
     pairs_chunk = [visible_pairs(cu_q, c.cu_k, q_off, c.k_off) for c in g.chunks]
@@ -115,55 +120,82 @@ def main() -> int:
     flops_step = sum(flops_chunk)
     tq = int(cu_q[-1])
     merge_bytes = 3 * (tq * w.hq * w.d * 4 + tq * w.hq * 4)
-    n_merge = len(g.chunks) - 1
+    n_merge = nch - 1
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    attn_ev = [[(ev(), ev()) for _ in g.chunks] for _ in range(args.steps)]
+    attn_ev = {m: [[(ev(), ev()) for _ in g.chunks] for _ in range(args.steps)] for m in cra.MODES}
     merge_ev = [[(ev(), ev()) for _ in range(n_merge)] for _ in range(args.steps)]
 
-    def step(i=None):
-        for c in range(len(g.chunks)):
-            out, lse = (bufs.o_acc, bufs.lse_acc) if c == 0 else (bufs.o_part, bufs.lse_part)
-            if i is not None:
-                attn_ev[i][c][0].record(stream)
-            cra.cpattn_fwd_chunk(q, ks[c], vs[c], cu_q, cu_ks[c], q_off, k_offs[c], True, out=out,
-                                 lse=lse, workspace=bufs.workspace, stream=stream)
-            if i is not None:
-                attn_ev[i][c][1].record(stream)
-            if c > 0:
-                if i is not None:
-                    merge_ev[i][c - 1][0].record(stream)
-                cra.cpattn_merge(bufs.o_acc, bufs.lse_acc, bufs.o_part, bufs.lse_part, stream=stream)
-                if i is not None:
-                    merge_ev[i][c - 1][1].record(stream)
+    spare_attn = [(ev(), ev()) for _ in g.chunks]        # recorded during warm-up, unread
+    spare_merge = [(ev(), ev()) for _ in range(n_merge)]
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_start, t_end = ev(), ev()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
+    def step(mode, a_ev, m_ev):
+        if mode == "stream":
+            a_ev[0][0].record(stream)
+            cra.cpattn_fwd_chunks(q, ks, vs, cu_q, cu_ks, q_off, k_offs, True, out=bufs.o_acc,
+                                  lse=bufs.lse_acc, workspace=bufs.workspace, stream=stream)
+            a_ev[0][1].record(stream)
+            return
+        for c in range(nch):
+            first = c == 0
+            out, lse = ((bufs.o_acc, bufs.lse_acc) if first or mode == "accum"
+                        else (bufs.o_part, bufs.lse_part))
+            fn = cra.cpattn_fwd_chunk if first or mode == "merge" else cra.cpattn_fwd_chunk_accum
+            a_ev[c][0].record(stream)
+            fn(q, ks[c], vs[c], cu_q, cu_ks[c], q_off, k_offs[c], True, out=out, lse=lse,
+               workspace=bufs.workspace, stream=stream)
+            a_ev[c][1].record(stream)
+            if mode == "merge" and not first:
+                m_ev[c - 1][0].record(stream)
+                cra.cpattn_merge(bufs.o_acc, bufs.lse_acc, bufs.o_part, bufs.lse_part, stream=stream)
+                m_ev[c - 1][1].record(stream)
+
+    def timed(mode):
+        for _ in range(args.warmup):
+            step(mode, spare_attn, spare_merge)
+        torch.cuda.synchronize()
+        # A full collection of the interpreter's heap takes tens of ms and would leave the GPU
+        # idle mid-step: collect now, freeze what exists, and keep the collector off while timing.
+        gc.collect()
+        gc.freeze()
+        gc.disable()
+        try:
+            t_start, t_end = ev(), ev()
+            t_start.record(stream)
+            for i in range(args.steps):
+                step(mode, attn_ev[mode][i], merge_ev[i])
+            t_end.record(stream)
+            torch.cuda.synchronize()
+        finally:
+            gc.enable()
+            gc.unfreeze()
+        return t_start.elapsed_time(t_end) / args.steps
+
+    schedules = {}
+    for mode in ("merge", "accum", "stream"):   # the headline schedule last, on a warm GPU
+        ms = timed(mode)
+        launches = 1 if mode == "stream" else nch
+        a_ms = sum(row[c][0].elapsed_time(row[c][1]) for row in attn_ev[mode]
+                   for c in range(launches)) / (args.steps * launches)
+        schedules[mode] = {"ms_per_step": round(ms, 4),
+                           "tflops": round(flops_step / (ms / 1e3) / 1e12, 2),
+                           "attn_launches_per_step": launches,
+                           "attn_avg_launch_us": round(a_ms * 1e3, 2)}
+    ms_step = schedules["stream"]["ms_per_step"]
     value = flops_step / (ms_step / 1e3) / 1e12
 
-    attn_ms = sum(a.elapsed_time(b) for row in attn_ev for a, b in row)
-    merge_ms = sum(a.elapsed_time(b) for row in merge_ev for a, b in row)
-    n_attn = args.steps * len(g.chunks)
-    attn_avg_ms = attn_ms / n_attn
-    attn_flops_per_launch = flops_step / len(g.chunks)
+    attn_avg_ms = schedules["stream"]["attn_avg_launch_us"] / 1e3
+    attn_flops_per_launch = flops_step
     attn_tflops = attn_flops_per_launch / (attn_avg_ms / 1e3) / 1e12
+    merge_ms = sum(a.elapsed_time(b) for row in merge_ev for a, b in row)
     merge_avg_ms = merge_ms / max(1, args.steps * n_merge)
     merge_gbs = merge_bytes / (merge_avg_ms / 1e3) / 1e9 if n_merge else None
 
     import hashlib
     with open(ATTN_SOURCE, "rb") as f:
         traffic = PROFILED_TRAFFIC.get(hashlib.sha256(f.read()).hexdigest())
-    tk = int(cu_ks[0][-1])
-    attn_bytes = tq * w.hq * w.d * 2 + 2 * tk * w.hkv * w.d * 2 + tq * w.hq * w.d * 4 + tq * w.hq * 4
+    tk_all = sum(int(c[-1]) for c in cu_ks)
+    attn_bytes = tq * w.hq * w.d * 2 + 2 * tk_all * w.hkv * w.d * 2 + tq * w.hq * w.d * 4 + tq * w.hq * 4
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -179,7 +211,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{w.name} (seed {w.seed}): last CP4 rank of a 16,384-token THD "
                                f"pack, local Q {tq} tokens in {len(cu_q) - 1} sequences, "
-                               f"{len(g.chunks)} KV chunks of {int(cu_ks[0][-1])} tokens, "
+                               f"{nch} KV chunks of {int(cu_ks[0][-1])} tokens, "
                                f"{w.hq}/{w.hkv} heads, D={w.d}, causal",
                    "global_batch": 16384, "seq_len": int(max(w.lengths)), "parallelism": "cp4-share"},
         "mfma_util": round(value / BF16_PEAK_TFLOPS, 4),
@@ -188,11 +220,12 @@ def main() -> int:
                      "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)",
                      "algorithmic_bytes_per_launch": attn_bytes,
-                     "kernel": "attn_fwd_bf16_kernel<128> (event-timed per cpattn_fwd_chunk call, "
-                               "plan upload included)",
+                     "kernel": "attn_fwd_bf16_kernel<128,false> over all chunks (event-timed per "
+                               "cpattn_fwd_chunks call, plan upload included)",
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
                      "flops_per_launch": attn_flops_per_launch},
-        "merge": {"avg_launch_us": round(merge_avg_ms * 1e3, 2) if n_merge else None,
+        "schedules": schedules,
+        "merge": {"schedule": "merge", "avg_launch_us": round(merge_avg_ms * 1e3, 2) if n_merge else None,
                   "bytes_per_launch": merge_bytes, "achieved_GBs": round(merge_gbs, 1) if merge_gbs else None,
                   "hbm_frac": round(merge_gbs / HBM_PEAK_GBS, 4) if merge_gbs else None},
         "flops_per_step": flops_step,

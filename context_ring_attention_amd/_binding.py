@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
-from typing import Optional, Tuple
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -22,8 +22,10 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1
 
 # Every symbol include/cpattn.h declares.
-EXPORTED = ("cpattn_workspace_size", "cpattn_fwd_chunk", "cpattn_merge", "cpattn_status_string",
-            "cpattn_last_error", "cpattn_plan_build")
+EXPORTED = ("cpattn_workspace_size", "cpattn_workspace_size_chunks", "cpattn_fwd_chunk",
+            "cpattn_fwd_chunk_accum", "cpattn_fwd_chunks", "cpattn_merge", "cpattn_status_string",
+            "cpattn_last_error", "cpattn_plan_build", "cpattn_plan_build_chunks")
+MAX_CHUNKS = 16  # CPATTN_MAX_CHUNKS
 
 
 class CpattnError(RuntimeError):
@@ -40,7 +42,8 @@ class PlanEntry(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("n_entries", c_int32), ("n_tiles", c_int32), ("tokens_per_tile", c_int32),
                 ("heads_per_tile", c_int32), ("head_groups", c_int32), ("block_n", c_int32),
-                ("visible_pairs", c_int64), ("key_blocks", c_int64), ("plan_bytes", c_size_t)]
+                ("visible_pairs", c_int64), ("key_blocks", c_int64), ("plan_bytes", c_size_t),
+                ("n_chunks", c_int32), ("reserved", c_int32)]
 
 
 PLAN_DTYPE = np.dtype([(name, np.int32) for name, _ in PlanEntry._fields_])
@@ -59,10 +62,19 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     lib.cpattn_workspace_size.restype = c_size_t
     lib.cpattn_workspace_size.argtypes = [c_int32, _I32P, c_int32, c_int32, c_int32]
-    lib.cpattn_fwd_chunk.restype = c_int
-    lib.cpattn_fwd_chunk.argtypes = [c_void_p, c_void_p, c_void_p, _I32P, _I32P, _I32P, _I32P,
-                                     c_int32, c_int32, c_int32, c_int32, c_int, c_int32,
-                                     c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.cpattn_workspace_size_chunks.restype = c_size_t
+    lib.cpattn_workspace_size_chunks.argtypes = [c_int32, _I32P, c_int32, c_int32, c_int32, c_int32]
+    for name in ("cpattn_fwd_chunk", "cpattn_fwd_chunk_accum"):
+        fn = getattr(lib, name)
+        fn.restype = c_int
+        fn.argtypes = [c_void_p, c_void_p, c_void_p, _I32P, _I32P, _I32P, _I32P, c_int32, c_int32,
+                       c_int32, c_int32, c_int, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
+                       c_void_p]
+    lib.cpattn_fwd_chunks.restype = c_int
+    lib.cpattn_fwd_chunks.argtypes = [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int32,
+                                      _I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
+                                      c_int32, c_int, c_int32, c_int32, c_void_p, c_void_p,
+                                      c_void_p, c_size_t, c_void_p]
     lib.cpattn_merge.restype = c_int
     lib.cpattn_merge.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32,
                                  c_void_p]
@@ -74,6 +86,10 @@ def load(path: str = LIB_PATH):
     lib.cpattn_plan_build.argtypes = [_I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
                                       c_int32, c_int, c_int32, c_void_p, c_size_t,
                                       POINTER(PlanInfo)]
+    lib.cpattn_plan_build_chunks.restype = c_int
+    lib.cpattn_plan_build_chunks.argtypes = [_I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
+                                             c_int32, c_int32, c_int, c_int32, c_void_p, c_size_t,
+                                             POINTER(PlanInfo)]
     _lib = lib
     return lib
 
@@ -117,9 +133,46 @@ def cpattn_workspace_size(nseq: int, cu_seqlens_q, hq: int, hkv: int, d: int) ->
     return int(load().cpattn_workspace_size(nseq, ptr, hq, hkv, d))
 
 
+def _chunk_meta(cu_seqlens_ks: Sequence, k_pos_offsets: Optional[Sequence], nseq: int):
+    """Host [nchunks][nseq + 1] cu_seqlens and [nchunks][nseq] offsets (or None), int32."""
+    nchunks = len(cu_seqlens_ks)
+    ck = np.stack([_host_i32(c, nseq + 1, "cu_seqlens_k")[0] for c in cu_seqlens_ks]) \
+        if nchunks else np.zeros((0, nseq + 1), np.int32)
+    ck = np.ascontiguousarray(ck, np.int32)
+    if k_pos_offsets is None or all(o is None for o in k_pos_offsets):
+        return ck, None
+    ko = np.stack([np.zeros(nseq, np.int32) if o is None else _host_i32(o, nseq, "k_pos_offset")[0]
+                   for o in k_pos_offsets])
+    return ck, np.ascontiguousarray(ko, np.int32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_I32P)
+
+
+def cpattn_plan_build_chunks(cu_seqlens_q, cu_seqlens_ks: Sequence, q_pos_offset=None,
+                             k_pos_offsets: Optional[Sequence] = None, *, hq: int, hkv: int, d: int,
+                             dtype: int = BF16, causal: bool = True):
+    """Host-only plan over several chunks: (entries [n_tiles * nchunks], info dict)."""
+    cq, pq = _host_i32(cu_seqlens_q, None, "cu_seqlens_q")
+    nseq = len(cq) - 1
+    qo, pqo = _host_i32(q_pos_offset, nseq, "q_pos_offset")
+    ck, ko = _chunk_meta(cu_seqlens_ks, k_pos_offsets, nseq)
+    lib = load()
+    info = PlanInfo()
+    nch = len(cu_seqlens_ks)
+    _check(lib.cpattn_plan_build_chunks(pq, _ptr(ck), pqo, _ptr(ko), nch, nseq, hq, hkv, d, dtype,
+                                        int(causal), None, 0, ctypes.byref(info)))
+    entries = np.zeros(info.n_entries, dtype=PLAN_DTYPE)
+    _check(lib.cpattn_plan_build_chunks(pq, _ptr(ck), pqo, _ptr(ko), nch, nseq, hq, hkv, d, dtype,
+                                        int(causal), c_void_p(entries.ctypes.data), entries.nbytes,
+                                        ctypes.byref(info)))
+    return entries, {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+
+
 def cpattn_plan_build(cu_seqlens_q, cu_seqlens_k, q_pos_offset=None, k_pos_offset=None, *,
                       hq: int, hkv: int, d: int, dtype: int = BF16, causal: bool = True):
-    """Host-only plan: (entries as a numpy structured array, info dict)."""
+    """Host-only plan of one chunk: (entries as a numpy structured array, info dict)."""
     cq, pq = _host_i32(cu_seqlens_q, None, "cu_seqlens_q")
     nseq = len(cq) - 1
     ck, pk = _host_i32(cu_seqlens_k, nseq + 1, "cu_seqlens_k")
@@ -135,14 +188,35 @@ def cpattn_plan_build(cu_seqlens_q, cu_seqlens_k, q_pos_offset=None, k_pos_offse
     return entries, {name: getattr(info, name) for name, _ in PlanInfo._fields_}
 
 
-def cpattn_fwd_chunk(q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos_offset=None, k_pos_offset=None,
-                     causal: bool = True, out=None, lse=None, workspace=None,
-                     stream=None) -> Tuple["object", "object"]:
-    """One KV chunk -> (O [Tq, Hq, D] fp32, LSE [Hq, Tq] fp32), asynchronously on the stream.
+def cpattn_workspace_size_chunks(nseq: int, cu_seqlens_q, hq: int, hkv: int, d: int,
+                                 nchunks: int) -> int:
+    arr, ptr = _host_i32(cu_seqlens_q, nseq + 1, "cu_seqlens_q")
+    return int(load().cpattn_workspace_size_chunks(nseq, ptr, hq, hkv, d, nchunks))
 
-    q [Tq, Hq, D], k/v [Tk, Hkv, D]: contiguous CUDA tensors, bfloat16 or float32.
-    cu_seqlens_*, *_pos_offset: host metadata (numpy / list / CPU tensor), int32.
-    """
+
+def _check_tensor(name, t):
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [T, H, D]")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA tensor")
+
+
+def _outputs(q, out, lse):
+    import torch
+    tq, hq, d = q.shape
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    if out.shape != (tq, hq, d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [Tq, Hq, D] tensor")
+    if lse.shape != (hq, tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [Hq, Tq] tensor")
+    return out, lse
+
+
+def _fwd_one(fn_name, q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, causal,
+             out, lse, workspace, stream):
     import torch
     lib = load()
     cq, pq = _host_i32(cu_seqlens_q, None, "cu_seqlens_q")
@@ -150,11 +224,8 @@ def cpattn_fwd_chunk(q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos_offset=None, k_p
     ck, pk = _host_i32(cu_seqlens_k, nseq + 1, "cu_seqlens_k")
     qo, pqo = _host_i32(q_pos_offset, nseq, "q_pos_offset")
     ko, pko = _host_i32(k_pos_offset, nseq, "k_pos_offset")
-    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
-        raise ValueError("q, k, v must be [T, H, D]")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+        _check_tensor(name, t)
     dt = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
@@ -164,22 +235,93 @@ def cpattn_fwd_chunk(q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos_offset=None, k_p
         raise ValueError("k and v must be [Tk, Hkv, D] with Q's D")
     if int(cq[-1]) != tq or int(ck[-1]) != tk:
         raise ValueError("cu_seqlens must end at the row counts of q and k")
-    if out is None:
-        out = torch.empty((tq, hq, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
-    if out.shape != (tq, hq, d) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [Tq, Hq, D] tensor")
-    if lse.shape != (hq, tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [Hq, Tq] tensor")
+    out, lse = _outputs(q, out, lse)
     need = lib.cpattn_workspace_size(nseq, pq, hq, hkv, d)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(lib.cpattn_fwd_chunk(c_void_p(q.data_ptr()), c_void_p(k.data_ptr()),
-                                c_void_p(v.data_ptr()), pq, pk, pqo, pko, nseq, hq, hkv, d, dt,
-                                int(causal), c_void_p(out.data_ptr()), c_void_p(lse.data_ptr()),
-                                c_void_p(workspace.data_ptr()), workspace.numel(),
-                                _stream_handle(stream)))
+    _check(getattr(lib, fn_name)(c_void_p(q.data_ptr()), c_void_p(k.data_ptr()),
+                                 c_void_p(v.data_ptr()), pq, pk, pqo, pko, nseq, hq, hkv, d, dt,
+                                 int(causal), c_void_p(out.data_ptr()), c_void_p(lse.data_ptr()),
+                                 c_void_p(workspace.data_ptr()), workspace.numel(),
+                                 _stream_handle(stream)))
+    return out, lse
+
+
+def cpattn_fwd_chunk(q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos_offset=None, k_pos_offset=None,
+                     causal: bool = True, out=None, lse=None, workspace=None,
+                     stream=None) -> Tuple["object", "object"]:
+    """One KV chunk -> (O [Tq, Hq, D] fp32, LSE [Hq, Tq] fp32), asynchronously on the stream.
+
+    q [Tq, Hq, D], k/v [Tk, Hkv, D]: contiguous CUDA tensors, bfloat16 or float32.
+    cu_seqlens_*, *_pos_offset: host metadata (numpy / list / CPU tensor), int32.
+    """
+    return _fwd_one("cpattn_fwd_chunk", q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos_offset,
+                    k_pos_offset, causal, out, lse, workspace, stream)
+
+
+def cpattn_fwd_chunk_accum(q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos_offset=None,
+                           k_pos_offset=None, causal: bool = True, out=None, lse=None,
+                           workspace=None, stream=None) -> Tuple["object", "object"]:
+    """(out, lse) <- merge((out, lse), partial of this chunk); out/lse are required."""
+    if out is None or lse is None:
+        raise ValueError("cpattn_fwd_chunk_accum folds into existing out and lse tensors")
+    return _fwd_one("cpattn_fwd_chunk_accum", q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos_offset,
+                    k_pos_offset, causal, out, lse, workspace, stream)
+
+
+def cpattn_fwd_chunks(q, ks: Sequence, vs: Sequence, cu_seqlens_q, cu_seqlens_ks: Sequence,
+                      q_pos_offset=None, k_pos_offsets: Optional[Sequence] = None,
+                      causal: bool = True, accumulate: bool = False, out=None, lse=None,
+                      workspace=None, stream=None) -> Tuple["object", "object"]:
+    """All KV chunks in one launch -> (O, LSE) over the union of their keys.
+
+    ks[c], vs[c]: chunk c's [Tk_c, Hkv, D] CUDA tensors; cu_seqlens_ks[c], k_pos_offsets[c]: its
+    host metadata.  accumulate=True folds the result into the given out/lse.
+    """
+    import torch
+    lib = load()
+    nch = len(ks)
+    if nch != len(vs) or nch != len(cu_seqlens_ks):
+        raise ValueError("ks, vs and cu_seqlens_ks must have one entry per chunk")
+    if k_pos_offsets is not None and len(k_pos_offsets) != nch:
+        raise ValueError("k_pos_offsets must have one entry per chunk")
+    cq, pq = _host_i32(cu_seqlens_q, None, "cu_seqlens_q")
+    nseq = len(cq) - 1
+    qo, pqo = _host_i32(q_pos_offset, nseq, "q_pos_offset")
+    ck, ko = _chunk_meta(cu_seqlens_ks, k_pos_offsets, nseq)
+    _check_tensor("q", q)
+    dt = _dtype_code(q)
+    tq, hq, d = q.shape
+    if int(cq[-1]) != tq:
+        raise ValueError("cu_seqlens_q must end at the row count of q")
+    hkv = None
+    for c in range(nch):
+        _check_tensor(f"ks[{c}]", ks[c])
+        _check_tensor(f"vs[{c}]", vs[c])
+        if ks[c].dtype != q.dtype or vs[c].dtype != q.dtype:
+            raise TypeError("q and every chunk's k, v must share one dtype")
+        if vs[c].shape != ks[c].shape or ks[c].shape[2] != d:
+            raise ValueError("k and v must be [Tk, Hkv, D] with Q's D")
+        if hkv is not None and ks[c].shape[1] != hkv:
+            raise ValueError("every chunk must have the same kv head count")
+        hkv = ks[c].shape[1]
+        if int(ck[c, -1]) != ks[c].shape[0]:
+            raise ValueError(f"cu_seqlens_ks[{c}] must end at chunk {c}'s row count")
+    if hkv is None:
+        raise ValueError("need at least one chunk")
+    if accumulate and (out is None or lse is None):
+        raise ValueError("accumulate=True folds into existing out and lse tensors")
+    out, lse = _outputs(q, out, lse)
+    need = lib.cpattn_workspace_size_chunks(nseq, pq, hq, hkv, d, nch)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    kp = (c_void_p * max(nch, 1))(*[t.data_ptr() for t in ks])
+    vp = (c_void_p * max(nch, 1))(*[t.data_ptr() for t in vs])
+    _check(lib.cpattn_fwd_chunks(c_void_p(q.data_ptr()), kp, vp, nch, pq, _ptr(ck), pqo, _ptr(ko),
+                                 nseq, hq, hkv, d, dt, int(causal), int(accumulate),
+                                 c_void_p(out.data_ptr()), c_void_p(lse.data_ptr()),
+                                 c_void_p(workspace.data_ptr()), workspace.numel(),
+                                 _stream_handle(stream)))
     return out, lse
 
 

@@ -116,35 +116,44 @@ const char* cpattn_status_string(cpattn_status s) {
 
 const char* cpattn_last_error(void) { return last_error_text(); }
 
-size_t cpattn_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q, int32_t hq, int32_t hkv,
-                             int32_t d) {
+size_t cpattn_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_q, int32_t hq,
+                                    int32_t hkv, int32_t d, int32_t nchunks) {
   (void)d;
   if (nseq < 0 || hq < 1 || hkv < 1 || (nseq > 0 && !cu_seqlens_q)) return 0;
+  if (nchunks < 1 || nchunks > CPATTN_MAX_CHUNKS) return 0;
   for (int32_t i = 0; i < nseq; ++i)
     if (cu_seqlens_q[i + 1] < cu_seqlens_q[i]) return 0;
-  // The smallest token block of any geometry bounds the entry count.
-  const int64_t n = count_entries(cu_seqlens_q, nseq, kMinTileTokens);
-  return std::max<size_t>(256, size_t(n) * sizeof(cpattn_plan_entry));
+  // The smallest token block of any geometry bounds the tile count.
+  const int64_t n = count_tiles(cu_seqlens_q, nseq, kMinTileTokens);
+  return std::max<size_t>(256, size_t(n) * nchunks * sizeof(cpattn_plan_entry));
 }
 
-cpattn_status cpattn_plan_build(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                                const int32_t* q_pos_offset, const int32_t* k_pos_offset,
-                                int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
-                                cpattn_dtype dtype, int32_t causal, cpattn_plan_entry* plan,
-                                size_t plan_bytes, cpattn_plan_info* info) {
+size_t cpattn_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q, int32_t hq, int32_t hkv,
+                             int32_t d) {
+  return cpattn_workspace_size_chunks(nseq, cu_seqlens_q, hq, hkv, d, 1);
+}
+
+cpattn_status cpattn_plan_build_chunks(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                       const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                       int32_t nchunks, int32_t nseq, int32_t hq, int32_t hkv,
+                                       int32_t d, cpattn_dtype dtype, int32_t causal,
+                                       cpattn_plan_entry* plan, size_t plan_bytes,
+                                       cpattn_plan_info* info) {
   clear_error();
   if (dtype != CPATTN_BF16 && dtype != CPATTN_FP32)
     return set_error(CPATTN_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   cpattn_status st = validate_metadata(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset,
-                                       nseq, hq, hkv, d);
+                                       nchunks, nseq, hq, hkv, d);
   if (st != CPATTN_OK) return st;
   const Geometry g = geometry_for(dtype, hq, hkv);
-  const int64_t n = count_entries(cu_seqlens_q, nseq, g.tokens_per_tile);
-  if (plan && plan_bytes < size_t(n) * sizeof(cpattn_plan_entry))
-    return set_error(CPATTN_ERR_WORKSPACE, "plan buffer of %zu bytes, need %zu", plan_bytes,
-                     size_t(n) * sizeof(cpattn_plan_entry));
-  build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq, causal, g, plan, n,
-                info);
+  const int64_t n = count_tiles(cu_seqlens_q, nseq, g.tokens_per_tile);
+  if (n * nchunks > int64_t(INT32_MAX))
+    return set_error(CPATTN_ERR_UNSUPPORTED, "too many plan entries");
+  const size_t need = size_t(n) * nchunks * sizeof(cpattn_plan_entry);
+  if (plan && plan_bytes < need)
+    return set_error(CPATTN_ERR_WORKSPACE, "plan buffer of %zu bytes, need %zu", plan_bytes, need);
+  build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal, g,
+                plan, n, info);
   if (info) {
     info->head_groups = hq / g.heads_per_tile;
     info->n_tiles = int32_t(n * info->head_groups);
@@ -152,62 +161,135 @@ cpattn_status cpattn_plan_build(const int32_t* cu_seqlens_q, const int32_t* cu_s
   return CPATTN_OK;
 }
 
-cpattn_status cpattn_fwd_chunk(const void* q, const void* k, const void* v,
-                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                               const int32_t* q_pos_offset, const int32_t* k_pos_offset,
-                               int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
-                               cpattn_dtype dtype, int32_t causal, float* o, float* lse,
-                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+cpattn_status cpattn_plan_build(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
+                                cpattn_dtype dtype, int32_t causal, cpattn_plan_entry* plan,
+                                size_t plan_bytes, cpattn_plan_info* info) {
+  return cpattn_plan_build_chunks(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, 1, nseq,
+                                  hq, hkv, d, dtype, causal, plan, plan_bytes, info);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared body of the three attention entry points.
+cpattn_status fwd_impl(const void* q, const void* const* ks, const void* const* vs,
+                       int32_t nchunks, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       const int32_t* q_pos_offset, const int32_t* k_pos_offset, int32_t nseq,
+                       int32_t hq, int32_t hkv, int32_t d, cpattn_dtype dtype, int32_t causal,
+                       int32_t accumulate, float* o, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
   clear_error();
   if (dtype != CPATTN_BF16 && dtype != CPATTN_FP32)
     return set_error(CPATTN_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  if (accumulate != 0 && accumulate != 1)
+    return set_error(CPATTN_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  if (nchunks >= 1 && nchunks <= CPATTN_MAX_CHUNKS && (!ks || !vs))
+    return set_error(CPATTN_ERR_INVALID_ARG, "chunk pointer arrays must be non-null");
   cpattn_status st = validate_metadata(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset,
-                                       nseq, hq, hkv, d);
+                                       nchunks, nseq, hq, hkv, d);
   if (st != CPATTN_OK) return st;
-  const int64_t tq = cu_seqlens_q[nseq], tk = cu_seqlens_k[nseq];
+  const int64_t tq = cu_seqlens_q[nseq];
   if (tq == 0) return CPATTN_OK;  // nothing to write
   const size_t esz = dtype == CPATTN_BF16 ? 2 : 4;
   if (!q || !o || !lse) return set_error(CPATTN_ERR_INVALID_ARG, "q, o and lse must be non-null");
-  if (tk > 0 && (!k || !v)) return set_error(CPATTN_ERR_INVALID_ARG, "k and v must be non-null");
-  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4) || (tk > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return set_error(CPATTN_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned and lse 4-byte aligned");
-  const size_t q_bytes = size_t(tq) * hq * d * esz, kv_bytes = size_t(tk) * hkv * d * esz;
+  const size_t q_bytes = size_t(tq) * hq * d * esz;
   const size_t o_bytes = size_t(tq) * hq * d * 4, lse_bytes = size_t(tq) * hq * 4;
-  if (overlaps(o, o_bytes, q, q_bytes) || overlaps(o, o_bytes, k, kv_bytes) ||
-      overlaps(o, o_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, o, o_bytes))
+  if (overlaps(o, o_bytes, q, q_bytes) || overlaps(lse, lse_bytes, o, o_bytes) ||
+      overlaps(lse, lse_bytes, q, q_bytes))
     return set_error(CPATTN_ERR_INVALID_ARG, "o/lse must not overlap q, k, v or each other");
+  for (int32_t c = 0; c < nchunks; ++c) {
+    const int64_t tk = cu_seqlens_k[int64_t(c) * (nseq + 1) + nseq];
+    if (tk == 0) continue;
+    if (!ks[c] || !vs[c])
+      return set_error(CPATTN_ERR_INVALID_ARG, "k and v must be non-null (chunk %d)", c);
+    if (!aligned(ks[c], 16) || !aligned(vs[c], 16))
+      return set_error(CPATTN_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned and lse 4-byte aligned");
+    const size_t kv_bytes = size_t(tk) * hkv * d * esz;
+    if (overlaps(o, o_bytes, ks[c], kv_bytes) || overlaps(o, o_bytes, vs[c], kv_bytes) ||
+        overlaps(lse, lse_bytes, ks[c], kv_bytes) || overlaps(lse, lse_bytes, vs[c], kv_bytes))
+      return set_error(CPATTN_ERR_INVALID_ARG, "o/lse must not overlap q, k, v or each other");
+  }
 
   const Geometry g = geometry_for(dtype, hq, hkv);
-  const int64_t n = count_entries(cu_seqlens_q, nseq, g.tokens_per_tile);
-  const size_t plan_bytes = size_t(n) * sizeof(cpattn_plan_entry);
+  const int64_t n = count_tiles(cu_seqlens_q, nseq, g.tokens_per_tile);
+  const size_t plan_bytes = size_t(n) * nchunks * sizeof(cpattn_plan_entry);
   if (!workspace || workspace_bytes < plan_bytes || !aligned(workspace, 256))
     return set_error(CPATTN_ERR_WORKSPACE, "workspace of %zu bytes (need %zu, 256-byte aligned)",
                      workspace_bytes, plan_bytes);
   const int head_groups = hq / g.heads_per_tile;
-  if (n * head_groups > int64_t(INT32_MAX))
+  if (n * head_groups > int64_t(INT32_MAX) || n * nchunks > int64_t(INT32_MAX))
     return set_error(CPATTN_ERR_UNSUPPORTED, "too many tiles for one launch");
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
     return set_error(CPATTN_ERR_HIP, "hipGetDevice failed");
   st = g_rings[dev].upload(workspace, plan_bytes, stream, [&](char* dst) {
-    build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq, causal, g,
-                  reinterpret_cast<cpattn_plan_entry*>(dst), n, nullptr);
+    build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal,
+                  g, reinterpret_cast<cpattn_plan_entry*>(dst), n, nullptr);
   });
   if (st != CPATTN_OK) return st;
   const auto* plan = static_cast<const cpattn_plan_entry*>(workspace);
   hipError_t err;
   if (dtype == CPATTN_BF16) {
-    err = launch_attn_fwd_bf16(q, k, v, plan, int(n), head_groups, g.heads_per_tile, hq, hkv, d,
-                               int(tq), o, lse, stream);
+    ChunkPtrs<__bf16> kv{};
+    for (int32_t c = 0; c < nchunks; ++c) {
+      kv.k[c] = static_cast<const __bf16*>(ks[c]);
+      kv.v[c] = static_cast<const __bf16*>(vs[c]);
+    }
+    err = launch_attn_fwd_bf16(q, kv, nchunks, plan, int(n), head_groups, g.heads_per_tile, hq,
+                               hkv, d, int(tq), accumulate != 0, o, lse, stream);
   } else {
-    err = launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                              static_cast<const float*>(v), plan, int(n), hq, hkv, d, int(tq), o,
-                              lse, stream);
+    ChunkPtrs<float> kv{};
+    for (int32_t c = 0; c < nchunks; ++c) {
+      kv.k[c] = static_cast<const float*>(ks[c]);
+      kv.v[c] = static_cast<const float*>(vs[c]);
+    }
+    err = launch_attn_fwd_f32(static_cast<const float*>(q), kv, nchunks, plan, int(n), hq, hkv, d,
+                              int(tq), accumulate != 0, o, lse, stream);
   }
   if (err != hipSuccess)
     return set_error(CPATTN_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
   return CPATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cpattn_status cpattn_fwd_chunk(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                               int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
+                               cpattn_dtype dtype, int32_t causal, float* o, float* lse,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(q, &k, &v, 1, cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq, hq,
+                  hkv, d, dtype, causal, 0, o, lse, workspace, workspace_bytes, stream);
+}
+
+cpattn_status cpattn_fwd_chunk_accum(const void* q, const void* k, const void* v,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                     int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
+                                     cpattn_dtype dtype, int32_t causal, float* o, float* lse,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(q, &k, &v, 1, cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq, hq,
+                  hkv, d, dtype, causal, 1, o, lse, workspace, workspace_bytes, stream);
+}
+
+cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void* const* vs,
+                                int32_t nchunks, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const int32_t* q_pos_offset,
+                                const int32_t* k_pos_offset, int32_t nseq, int32_t hq, int32_t hkv,
+                                int32_t d, cpattn_dtype dtype, int32_t causal, int32_t accumulate,
+                                float* o, float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  return fwd_impl(q, ks, vs, nchunks, cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq,
+                  hq, hkv, d, dtype, causal, accumulate, o, lse, workspace, workspace_bytes, stream);
 }
 
 cpattn_status cpattn_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,

@@ -3,11 +3,15 @@
 // One work-group = 4 waves = one tile of the host plan: up to 32 query tokens
 // per wave, for heads_per_tile query heads of one GQA group (the waves of a
 // tile share one kv head, so every K/V block staged in LDS serves all of them).
-// The kernel walks the tile's key blocks (64 keys each) of ONE KV chunk, keeps a
-// running max m and running sum l per query row (online softmax, the same
-// update as the ring loop of the "Megatron 6D parallelism guide", section 6,
-// applied across key blocks) and writes the normalised partial O = acc / l
-// and LSE = m + ln l of that chunk.
+// The kernel walks the tile's key blocks (64 keys each) of each of its KV
+// chunks in turn, keeps a running max m and running sum l per query row (online
+// softmax: the update of the ring loop of the "Megatron 6D parallelism guide",
+// section 6, applied across key blocks and across chunks alike) and at the end
+// writes the normalised O = acc / l and LSE = m + ln l of the tile's rows over
+// all those keys.  With one chunk that is the partial of that chunk.  In
+// accumulate mode the epilogue instead folds (O, LSE) into the running result
+// already in memory with the pages' merge (alpha, beta weights of the two
+// sides), so a ring step needs no separate merge pass.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64): the score tile is
 // computed transposed, S^T[key][token] = K * Q^T, so the 32x32 accumulator puts
@@ -27,7 +31,8 @@
 // zero with no branches.  16-byte chunks are XOR-swizzled by row (one pattern
 // for the K reads, another for the V transpose reads) against bank conflicts;
 // the swizzle is applied by choosing which global chunk each lane fetches.  Two
-// LDS stages: block j+1 is in flight while block j is computed; one barrier per
+// LDS stages: the next block (of the same chunk, or the first of the next chunk
+// the tile sees) is in flight while the current one is computed; one barrier per
 // block.
 //
 // Softmax: scores stay in raw units s = q.k; p = exp2(s * c - m * c) with
@@ -118,9 +123,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const __bf16* base, 
 }
 #endif
 
-template <int D>
+template <int D, bool ACCUM>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ q, const ChunkPtrs<__bf16> kv, int nchunks,
     const cpattn_plan_entry* __restrict__ plan, int head_groups, int heads_per_tile, int hq,
     int hkv, int tq_total, float scale, float scale_log2, float* __restrict__ o,
     float* __restrict__ lse) {
@@ -139,26 +144,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int b = blockIdx.x;
   const int e = b / head_groups;
   const int hg = b - e * head_groups;
-  const cpattn_plan_entry pe = plan[e];
+  const cpattn_plan_entry* tile = plan + int64_t(e) * nchunks;  // one entry per chunk
+  const int row0 = tile[0].row0, nrows = tile[0].nrows;
   const int head = hg * heads_per_tile + (wave % heads_per_tile);
   const int tok0 = (wave / heads_per_tile) * kBf16RowsPerWave;
   const int kvh = (hg * heads_per_tile) / (hq / hkv);  // shared by every head of the tile
-
-  // Per-wave key range (rows tok0 .. tok0 + rows_w - 1 of the tile).
-  const int rows_w = min(max(pe.nrows - tok0, 0), kBf16RowsPerWave);
-  int nblk_w = 0, nfull_w = 0;
-  if (rows_w > 0) {
-    const int kend = max(0, min(pe.k_len, pe.delta + tok0 + rows_w));
-    nblk_w = (kend + BN - 1) / BN;
-    nfull_w = min(min(pe.k_len / BN, max(0, pe.delta + tok0 + 1) / BN), nblk_w);
-  }
-  const int nblk = pe.cost;  // blocks the whole tile visits (uniform)
+  const int rows_w = min(max(nrows - tok0, 0), kBf16RowsPerWave);  // this wave's rows
 
   // Q fragment: B operand of S^T = K Q^T; lane holds Q[token n][16 ks + 8 g .. +7].
   bf16x8 qf[KS];
   {
     const bool ok = n < rows_w;
-    const __bf16* qp = q + (int64_t(pe.row0 + tok0 + n) * hq + head) * D + 8 * g;
+    const __bf16* qp = q + (int64_t(row0 + tok0 + n) * hq + head) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * ks) : bf16x8{};
@@ -172,15 +169,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const float thr = kRescaleLog2 / scale_log2;
 
   // ---- HBM -> LDS block loads (each wave fills kLoadsPerWave KB of K and of V) ----
+  // Block j of chunk c: rows k_start + 64 j .. of that chunk's K and V.
   const int64_t stride_bytes = int64_t(hkv) * D * 2;
-  const __bf16* kbase = k + (int64_t(pe.k_start) * hkv + kvh) * D;
-  const __bf16* vbase = v + (int64_t(pe.k_start) * hkv + kvh) * D;
-  auto issue = [&](int j, int stage) {
-    const int64_t rows_left = int64_t(pe.k_len) - int64_t(j) * BN;
-    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kbase + int64_t(j) * BN * hkv * D, rows_left,
-                                                stride_bytes, D * 2);
-    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vbase + int64_t(j) * BN * hkv * D, rows_left,
-                                                stride_bytes, D * 2);
+  auto issue = [&](int c, int j, int stage) {
+    const cpattn_plan_entry& pc_e = tile[c];
+    const int64_t first = (int64_t(pc_e.k_start) + int64_t(j) * BN) * hkv + kvh;
+    const int64_t rows_left = int64_t(pc_e.k_len) - int64_t(j) * BN;
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kv.k[c] + first * D, rows_left, stride_bytes, D * 2);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(kv.v[c] + first * D, rows_left, stride_bytes, D * 2);
     char* s = smem + stage * L::kStage;
 #pragma unroll
     for (int i = 0; i < L::kLoadsPerWave; ++i) {
@@ -206,129 +202,173 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   // address of V row 16 kk + 4 g + jr (+ 8 for the second half) at columns 32 dt + 16 h + 4 q.
   const int jr = (n & 15) >> 2, qq = n & 3, hh = n >> 4;
 
-  if (nblk > 0) issue(0, 0);
+  // Chunks the tile sees keys of (cost > 0), in order.
+  auto next_chunk = [&](int c) {
+    ++c;
+    while (c < nchunks && tile[c].cost == 0) ++c;
+    return c;
+  };
 
-  for (int j = 0; j < nblk; ++j) {
-    const int stage = j & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 1 < nblk) issue(j + 1, stage ^ 1);
-    if (j < nblk_w) {
-      const char* s = smem + stage * L::kStage;
-      // ---- S^T = K Q^T for 64 keys (two 32-key tiles) ----
-      // K fragments are read one k-step ahead of the MFMAs that consume them.
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
-      bf16x8 a0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][0]);
-      bf16x8 a1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][0]);
+  int stage = 0;
+  int c = next_chunk(-1);
+  if (c < nchunks) issue(c, 0, 0);
+  for (; c < nchunks;) {
+    const cpattn_plan_entry pe = tile[c];
+    const int cn = next_chunk(c);
+    // This wave's key range in chunk c.
+    int nblk_w = 0, nfull_w = 0;
+    if (rows_w > 0) {
+      const int kend = max(0, min(pe.k_len, pe.delta + tok0 + rows_w));
+      nblk_w = (kend + BN - 1) / BN;
+      nfull_w = min(min(pe.k_len / BN, max(0, pe.delta + tok0 + 1) / BN), nblk_w);
+    }
+    const int nblk = pe.cost;  // blocks the whole tile visits in chunk c (uniform)
+    for (int j = 0; j < nblk; ++j, stage ^= 1) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 1 < nblk) issue(c, j + 1, stage ^ 1);
+      else if (cn < nchunks) issue(cn, 0, stage ^ 1);
+      if (j < nblk_w) {
+        const char* s = smem + stage * L::kStage;
+        // ---- S^T = K Q^T for 64 keys (two 32-key tiles) ----
+        // K fragments are read one k-step ahead of the MFMAs that consume them.
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
+        bf16x8 a0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][0]);
+        bf16x8 a1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][0]);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 n0, n1;
-        if (ks + 1 < KS) {
-          n0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][ks + 1]);
-          n1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][ks + 1]);
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8 n0, n1;
+          if (ks + 1 < KS) {
+            n0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][ks + 1]);
+            n1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][ks + 1]);
+          }
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+          if (ks + 1 < KS) {
+            a0 = n0;
+            a1 = n1;
+          }
         }
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
-        if (ks + 1 < KS) {
-          a0 = n0;
-          a1 = n1;
+        // ---- mask (diagonal / ragged blocks only) ----
+        if (j >= nfull_w) {
+          // key (within block) of register r: 32 kt + 8 (r / 4) + 4 g + r % 4
+          const int lim = min(pe.k_len - 1, pe.delta + tok0 + n) - j * BN - 4 * g;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kin = 8 * (r >> 2) + (r & 3);
+            if (kin > lim) s0[r] = -INFINITY;
+            if (32 + kin > lim) s1[r] = -INFINITY;
+          }
         }
-      }
-      // ---- mask (diagonal / ragged blocks only) ----
-      if (j >= nfull_w) {
-        // key (within block) of register r: 32 kt + 8 (r / 4) + 4 g + r % 4
-        const int lim = min(pe.k_len - 1, pe.delta + tok0 + n) - j * BN - 4 * g;
+        // ---- online softmax ----
+        float mx;
+        {
+          float t[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) t[r] = __builtin_elementwise_max(s0[r], s1[r]);
+#pragma unroll
+          for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int r = 0; r < w; ++r) t[r] = __builtin_elementwise_max(t[r], t[r + w]);
+          mx = pair_max(t[0]);
+        }
+        if (__any(mx > m_run + thr)) {
+          const float m_new = __builtin_elementwise_max(m_run, mx);
+          const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+          const float alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * scale_log2);
+#pragma unroll
+          for (int i = 0; i < DT; ++i) acc[i] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
+        }
+        const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * scale_log2;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kin = 8 * (r >> 2) + (r & 3);
-          if (kin > lim) s0[r] = -INFINITY;
-          if (32 + kin > lim) s1[r] = -INFINITY;
+          s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, neg));
+          s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, neg));
         }
-      }
-      // ---- online softmax ----
-      float mx;
-      {
-        float t[16];
+        // P as bf16 B operands: key group kk takes registers 8 (kk % 2) .. +7 of tile kk / 2
+        bf16x8 pf[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) t[r] = __builtin_elementwise_max(s0[r], s1[r]);
+        for (int jj = 0; jj < 8; ++jj) {
+          pf[0][jj] = (__bf16)s0[jj];
+          pf[1][jj] = (__bf16)s0[8 + jj];
+          pf[2][jj] = (__bf16)s1[jj];
+          pf[3][jj] = (__bf16)s1[8 + jj];
+        }
+        {
+          const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+          float part[4];
 #pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
+          for (int kk = 0; kk < 4; ++kk) {
+            part[kk] = 0.f;
 #pragma unroll
-          for (int r = 0; r < w; ++r) t[r] = __builtin_elementwise_max(t[r], t[r + w]);
-        mx = pair_max(t[0]);
-      }
-      if (__any(mx > m_run + thr)) {
-        const float m_new = __builtin_elementwise_max(m_run, mx);
-        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * scale_log2);
-#pragma unroll
-        for (int i = 0; i < DT; ++i) acc[i] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-      }
-      const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * scale_log2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, neg));
-        s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, neg));
-      }
-      // P as bf16 B operands: key group kk takes registers 8 (kk % 2) .. +7 of tile kk / 2
-      bf16x8 pf[4];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        pf[0][jj] = (__bf16)s0[jj];
-        pf[1][jj] = (__bf16)s0[8 + jj];
-        pf[2][jj] = (__bf16)s1[jj];
-        pf[3][jj] = (__bf16)s1[8 + jj];
-      }
-      {
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-        float part[4];
+            for (int i = 0; i < 4; ++i)
+              part[kk] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[kk][2 * i], pf[kk][2 * i + 1]},
+                                                         ones, part[kk], false);
+          }
+          l_run += (part[0] + part[1]) + (part[2] + part[3]);
+        }
+        // ---- O^T += V^T P^T ----
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          part[kk] = 0.f;
+          const int row = 16 * kk + 4 * g + jr;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            part[kk] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[kk][2 * i], pf[kk][2 * i + 1]},
-                                                       ones, part[kk], false);
-        }
-        l_run += (part[0] + part[1]) + (part[2] + part[3]);
-      }
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int row = 16 * kk + 4 * g + jr;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int c16 = 4 * dt + 2 * hh + (qq >> 1);
-          const int off0 = L::v_off(row, c16) + 8 * (qq & 1);
-          const int off1 = L::v_off(row + 8, c16) + 8 * (qq & 1);
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off0));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off1));
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], acc[dt], 0, 0, 0);
+          for (int dt = 0; dt < DT; ++dt) {
+            const int c16 = 4 * dt + 2 * hh + (qq >> 1);
+            const int off0 = L::v_off(row, c16) + 8 * (qq & 1);
+            const int off1 = L::v_off(row + 8, c16) + 8 * (qq & 1);
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off0));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off1));
+            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], acc[dt], 0, 0, 0);
+          }
         }
       }
     }
+    c = cn;
   }
 
-  // ---- epilogue: O = acc / l, LSE = m * scale + ln l ----
+  // ---- epilogue: O = acc / l, LSE = m * scale + ln l (or their merge into o, lse) ----
   const float l_tot = pair_sum(l_run);
   if (n < rows_w) {
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    const int64_t row = pe.row0 + tok0 + n;
+    const int64_t row = row0 + tok0 + n;
     float* op = o + (row * hq + head) * D + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        float4 val = make_float4(acc[dt][4 * rq] * inv, acc[dt][4 * rq + 1] * inv,
-                                 acc[dt][4 * rq + 2] * inv, acc[dt][4 * rq + 3] * inv);
-        *reinterpret_cast<float4*>(op + 32 * dt + 8 * rq) = val;
+    float* lp = lse + int64_t(head) * tq_total + row;
+    const float lse_new = l_tot > 0.f ? m_run * scale + logf(l_tot) : -INFINITY;
+    float wa = 0.f, wb = l_tot > 0.f ? 1.0f / l_tot : 0.f, lse_out = lse_new;
+    bool write = true;
+    if (ACCUM) {
+      // (O, LSE) <- merge((O, LSE), (acc / l, lse_new)); an empty side leaves the other exact.
+      const float lse_old = *lp;
+      if (l_tot == 0.f) {
+        write = false;
+      } else if (lse_old != -INFINITY) {
+        const float mm = fmaxf(lse_old, lse_new);
+        const float alpha = expf(lse_old - mm), beta = expf(lse_new - mm);
+        const float inv = 1.0f / (alpha + beta);
+        wa = alpha * inv;
+        wb = beta * inv / l_tot;
+        lse_out = mm + logf(alpha + beta);
       }
     }
-    if (g == 0) {
-      lse[int64_t(head) * tq_total + row] = l_tot > 0.f ? m_run * scale + logf(l_tot) : -INFINITY;
+    if (write) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          float4* dst = reinterpret_cast<float4*>(op + 32 * dt + 8 * rq);
+          float4 val = make_float4(acc[dt][4 * rq] * wb, acc[dt][4 * rq + 1] * wb,
+                                   acc[dt][4 * rq + 2] * wb, acc[dt][4 * rq + 3] * wb);
+          if (ACCUM && wa != 0.f) {
+            const float4 old = *dst;
+            val = make_float4(fmaf(wa, old.x, val.x), fmaf(wa, old.y, val.y), fmaf(wa, old.z, val.z),
+                              fmaf(wa, old.w, val.w));
+          }
+          *dst = val;
+        }
+      }
+      if (g == 0) *lp = lse_out;
     }
   }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -336,23 +376,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
 }  // namespace
 
-hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v,
-                                const cpattn_plan_entry* plan, int n_entries, int head_groups,
-                                int heads_per_tile, int hq, int hkv, int d, int tq_total, float* o,
-                                float* lse, hipStream_t stream) {
-  if (n_entries == 0) return hipSuccess;
-  const dim3 grid(unsigned(n_entries) * unsigned(head_groups));
+hipError_t launch_attn_fwd_bf16(const void* q, const ChunkPtrs<__bf16>& kv, int nchunks,
+                                const cpattn_plan_entry* plan, int n_tiles, int head_groups,
+                                int heads_per_tile, int hq, int hkv, int d, int tq_total,
+                                bool accumulate, float* o, float* lse, hipStream_t stream) {
+  if (n_tiles == 0) return hipSuccess;
+  const dim3 grid(unsigned(n_tiles) * unsigned(head_groups));
   const float scale = 1.0f / sqrtf(float(d));
   const float scale_log2 = scale * 1.4426950408889634f;
   const auto* qb = static_cast<const __bf16*>(q);
-  const auto* kb = static_cast<const __bf16*>(k);
-  const auto* vb = static_cast<const __bf16*>(v);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, qb, kv, nchunks, plan, head_groups,
+                       heads_per_tile, hq, hkv, tq_total, scale, scale_log2, o, lse);
+  };
   if (d == 128) {
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(kThreads), 0, stream, qb, kb, vb, plan,
-                       head_groups, heads_per_tile, hq, hkv, tq_total, scale, scale_log2, o, lse);
+    if (accumulate) launch(attn_fwd_bf16_kernel<128, true>);
+    else launch(attn_fwd_bf16_kernel<128, false>);
   } else if (d == 64) {
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(kThreads), 0, stream, qb, kb, vb, plan,
-                       head_groups, heads_per_tile, hq, hkv, tq_total, scale, scale_log2, o, lse);
+    if (accumulate) launch(attn_fwd_bf16_kernel<64, true>);
+    else launch(attn_fwd_bf16_kernel<64, false>);
   } else {
     return hipErrorInvalidValue;
   }

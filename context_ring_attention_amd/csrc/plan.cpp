@@ -3,11 +3,12 @@
 // The causal mask is by global position (a query at q_pos sees keys with
 // k_pos <= q_pos of its own sequence), so under a KV chunk at offset k_off a
 // tile of query rows starting at q_off + row0 sees keys u <= delta + r with
-// delta = q_off + row0 - k_off.  The number of key blocks a tile visits is
-// therefore known on the host, and tiles are ordered longest first so that
-// the hardware's in-order work-group dispatch approximates longest-processing-
-// time scheduling of the causally unbalanced work (diagonal chunks give tiles
-// of 1..n blocks; sequences of a pack differ in length).
+// delta = q_off + row0 - k_off.  The number of key blocks a tile visits in each
+// chunk is therefore known on the host, and tiles are ordered by their total
+// over the chunks, longest first, so that the hardware's in-order work-group
+// dispatch approximates longest-processing-time scheduling of the causally
+// unbalanced work (diagonal chunks give tiles of 1..n blocks; sequences of a
+// pack differ in length).
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
@@ -44,9 +45,12 @@ Geometry geometry_for(cpattn_dtype dtype, int hq, int hkv) {
 }
 
 cpattn_status validate_metadata(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_off,
-                                const int32_t* k_off, int32_t nseq, int32_t hq, int32_t hkv,
-                                int32_t d) {
+                                const int32_t* k_off, int32_t nchunks, int32_t nseq, int32_t hq,
+                                int32_t hkv, int32_t d) {
   if (nseq < 0) return set_error(CPATTN_ERR_INVALID_ARG, "nseq must be >= 0 (got %d)", nseq);
+  if (nchunks < 1 || nchunks > CPATTN_MAX_CHUNKS)
+    return set_error(CPATTN_ERR_INVALID_ARG, "nchunks must be in 1..%d (got %d)", CPATTN_MAX_CHUNKS,
+                     nchunks);
   if (hq < 1 || hkv < 1) return set_error(CPATTN_ERR_INVALID_ARG, "hq and hkv must be >= 1");
   if (hq % hkv != 0)
     return set_error(CPATTN_ERR_INVALID_ARG, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
@@ -54,22 +58,36 @@ cpattn_status validate_metadata(const int32_t* cu_q, const int32_t* cu_k, const 
     return set_error(CPATTN_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
   if (!cu_q || !cu_k)
     return set_error(CPATTN_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be non-null");
-  if (cu_q[0] != 0 || cu_k[0] != 0)
-    return set_error(CPATTN_ERR_INVALID_ARG, "cu_seqlens must start at 0");
+  if (cu_q[0] != 0) return set_error(CPATTN_ERR_INVALID_ARG, "cu_seqlens must start at 0");
   for (int32_t i = 0; i < nseq; ++i) {
-    if (cu_q[i + 1] < cu_q[i] || cu_k[i + 1] < cu_k[i])
+    if (cu_q[i + 1] < cu_q[i])
       return set_error(CPATTN_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (sequence %d)", i);
-    const int64_t qo = q_off ? q_off[i] : 0, ko = k_off ? k_off[i] : 0;
-    if (qo < 0 || ko < 0)
-      return set_error(CPATTN_ERR_INVALID_ARG, "position offsets must be >= 0 (sequence %d)", i);
-    if (qo + (cu_q[i + 1] - cu_q[i]) > INT32_MAX || ko + (cu_k[i + 1] - cu_k[i]) > INT32_MAX)
+    const int64_t qo = q_off ? q_off[i] : 0;
+    if (qo < 0) return set_error(CPATTN_ERR_INVALID_ARG, "position offsets must be >= 0 (sequence %d)", i);
+    if (qo + (cu_q[i + 1] - cu_q[i]) > INT32_MAX)
       return set_error(CPATTN_ERR_INVALID_ARG, "positions of sequence %d overflow int32", i);
+  }
+  for (int32_t c = 0; c < nchunks; ++c) {
+    const int32_t* ck = cu_k + int64_t(c) * (nseq + 1);
+    const int32_t* ko_c = k_off ? k_off + int64_t(c) * nseq : nullptr;
+    if (ck[0] != 0) return set_error(CPATTN_ERR_INVALID_ARG, "cu_seqlens must start at 0 (chunk %d)", c);
+    for (int32_t i = 0; i < nseq; ++i) {
+      if (ck[i + 1] < ck[i])
+        return set_error(CPATTN_ERR_INVALID_ARG,
+                         "cu_seqlens must be non-decreasing (chunk %d, sequence %d)", c, i);
+      const int64_t ko = ko_c ? ko_c[i] : 0;
+      if (ko < 0)
+        return set_error(CPATTN_ERR_INVALID_ARG, "position offsets must be >= 0 (chunk %d, sequence %d)",
+                         c, i);
+      if (ko + (ck[i + 1] - ck[i]) > INT32_MAX)
+        return set_error(CPATTN_ERR_INVALID_ARG, "positions of chunk %d, sequence %d overflow int32", c, i);
+    }
   }
   // Element indices are computed in 64-bit inside the kernels; rows stay int32.
   return CPATTN_OK;
 }
 
-int64_t count_entries(const int32_t* cu_q, int32_t nseq, int tokens_per_tile) {
+int64_t count_tiles(const int32_t* cu_q, int32_t nseq, int tokens_per_tile) {
   int64_t n = 0;
   for (int32_t i = 0; i < nseq; ++i) {
     const int64_t len = int64_t(cu_q[i + 1]) - cu_q[i];
@@ -93,49 +111,64 @@ static int64_t visible_pairs(int64_t nq, int64_t nk, int64_t delta0, bool causal
 }
 
 void build_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_off,
-                   const int32_t* k_off, int32_t nseq, int32_t causal, const Geometry& g,
-                   cpattn_plan_entry* out, int64_t n, cpattn_plan_info* info) {
+                   const int32_t* k_off, int32_t nchunks, int32_t nseq, int32_t causal,
+                   const Geometry& g, cpattn_plan_entry* out, int64_t n_tiles,
+                   cpattn_plan_info* info) {
   const int tt = g.tokens_per_tile, bn = g.block_n;
-  std::vector<cpattn_plan_entry> tmp;
-  cpattn_plan_entry* dst = out;
-  if (!dst && info) { tmp.resize(size_t(n)); dst = tmp.data(); }
-  int64_t e = 0, pairs = 0, blocks = 0;
+  // Entries in (sequence, token block) order, chunk fastest.
+  std::vector<cpattn_plan_entry> ent(size_t(n_tiles) * nchunks);
+  std::vector<int64_t> total(size_t(n_tiles), 0);
+  int64_t t = 0, pairs = 0, blocks = 0;
   for (int32_t i = 0; i < nseq; ++i) {
-    const int32_t nq = cu_q[i + 1] - cu_q[i], nk = cu_k[i + 1] - cu_k[i];
-    const int64_t qo = q_off ? q_off[i] : 0, ko = k_off ? k_off[i] : 0;
-    if (info) pairs += visible_pairs(nq, nk, qo - ko, causal != 0);
-    for (int32_t tb = 0; tb * int64_t(tt) < nq; ++tb) {
-      cpattn_plan_entry p;
-      p.row0 = cu_q[i] + tb * tt;
-      p.nrows = std::min<int32_t>(tt, nq - tb * tt);
-      p.k_start = cu_k[i];
-      p.k_len = nk;
-      int64_t delta = causal ? (qo + int64_t(tb) * tt - ko) : int64_t(nk);
-      delta = std::max<int64_t>(-tt, std::min<int64_t>(delta, nk));
-      p.delta = int32_t(delta);
-      const int64_t kend = std::max<int64_t>(0, std::min<int64_t>(nk, delta + p.nrows));
-      p.cost = int32_t((kend + bn - 1) / bn);
-      p.seq = i;
-      p.tblock = tb;
-      if (dst) dst[e] = p;
-      blocks += p.cost;
-      ++e;
+    const int32_t nq = cu_q[i + 1] - cu_q[i];
+    const int64_t qo = q_off ? q_off[i] : 0;
+    for (int32_t c = 0; c < nchunks; ++c) {
+      const int32_t* ck = cu_k + int64_t(c) * (nseq + 1);
+      const int64_t ko = k_off ? k_off[int64_t(c) * nseq + i] : 0;
+      if (info) pairs += visible_pairs(nq, ck[i + 1] - ck[i], qo - ko, causal != 0);
+    }
+    for (int32_t tb = 0; tb * int64_t(tt) < nq; ++tb, ++t) {
+      for (int32_t c = 0; c < nchunks; ++c) {
+        const int32_t* ck = cu_k + int64_t(c) * (nseq + 1);
+        const int32_t nk = ck[i + 1] - ck[i];
+        const int64_t ko = k_off ? k_off[int64_t(c) * nseq + i] : 0;
+        cpattn_plan_entry p;
+        p.row0 = cu_q[i] + tb * tt;
+        p.nrows = std::min<int32_t>(tt, nq - tb * tt);
+        p.k_start = ck[i];
+        p.k_len = nk;
+        int64_t delta = causal ? (qo + int64_t(tb) * tt - ko) : int64_t(nk);
+        delta = std::max<int64_t>(-tt, std::min<int64_t>(delta, nk));
+        p.delta = int32_t(delta);
+        const int64_t kend = std::max<int64_t>(0, std::min<int64_t>(nk, delta + p.nrows));
+        p.cost = int32_t((kend + bn - 1) / bn);
+        p.seq = i;
+        p.tblock = tb;
+        ent[size_t(t) * nchunks + c] = p;
+        total[size_t(t)] += p.cost;
+        blocks += p.cost;
+      }
     }
   }
-  if (dst) {
+  if (out) {
     // Longest first; ties keep (sequence, token block) order so plans are deterministic.
-    std::stable_sort(dst, dst + n, [](const cpattn_plan_entry& a, const cpattn_plan_entry& b) {
-      return a.cost > b.cost;
-    });
+    std::vector<int64_t> order(static_cast<size_t>(n_tiles));
+    std::iota(order.begin(), order.end(), int64_t(0));
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int64_t a, int64_t b) { return total[size_t(a)] > total[size_t(b)]; });
+    for (int64_t k = 0; k < n_tiles; ++k)
+      std::copy_n(ent.begin() + order[size_t(k)] * nchunks, nchunks, out + k * nchunks);
   }
   if (info) {
-    info->n_entries = int32_t(n);
+    info->n_entries = int32_t(n_tiles * nchunks);
+    info->n_chunks = nchunks;
+    info->reserved = 0;
     info->tokens_per_tile = tt;
     info->heads_per_tile = g.heads_per_tile;
     info->block_n = bn;
     info->visible_pairs = pairs;
     info->key_blocks = blocks;
-    info->plan_bytes = size_t(n) * sizeof(cpattn_plan_entry);
+    info->plan_bytes = size_t(n_tiles) * nchunks * sizeof(cpattn_plan_entry);
   }
 }
 

@@ -67,6 +67,18 @@ typedef enum {
 size_t cpattn_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q, int32_t hq, int32_t hkv,
                              int32_t d);
 
+/* Most KV chunks one cpattn_fwd_chunks call takes (the pages' CP sizes are 1..8). */
+#define CPATTN_MAX_CHUNKS 16
+
+/*
+ * Bytes of device workspace one cpattn_fwd_chunks call with nchunks chunks needs
+ * (the work plan holds one record per tile and chunk).  nchunks == 1 gives
+ * cpattn_workspace_size().  Returns 0 for invalid arguments, including nchunks
+ * outside 1 .. CPATTN_MAX_CHUNKS.
+ */
+size_t cpattn_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_q, int32_t hq,
+                                    int32_t hkv, int32_t d, int32_t nchunks);
+
 /*
  * One KV chunk: the flash-attention partial of the pages' ring loop
  * ("Megatron 6D parallelism guide", section 6, the per-step call that returns
@@ -95,6 +107,54 @@ cpattn_status cpattn_fwd_chunk(const void* q, const void* k, const void* v,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Accumulating form of cpattn_fwd_chunk: the chunk's partial is folded into the
+ * running result in the kernel's epilogue instead of being written out,
+ *     (o, lse) <- merge((o, lse), partial of this chunk)
+ * with the merge of cpattn_merge below ("Megatron 6D parallelism guide", section
+ * 6: the online-softmax update applied once per ring step).  o and lse are read
+ * and written (device, same shapes as cpattn_fwd_chunk); a first call on a fresh
+ * result starts from O = 0, LSE = -inf everywhere.  Rows the chunk shows no key
+ * keep their values exactly; rows whose running LSE is -inf take the partial
+ * exactly.  Other arguments, ownership and errors as cpattn_fwd_chunk.
+ */
+cpattn_status cpattn_fwd_chunk_accum(const void* q, const void* k, const void* v,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                     int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
+                                     cpattn_dtype dtype, int32_t causal, float* o, float* lse,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Every KV chunk of a rank's share in ONE launch: the ring loop of the pages
+ * ("Megatron 6D parallelism guide", section 6) for chunks that are all resident,
+ * with the running max, running sum and accumulator of each query row carried
+ * across chunks in registers, so no partial is written and no merge pass runs.
+ * The result equals merging the nchunks partials of cpattn_fwd_chunk (up to
+ * rounding), i.e. attention of each query over the union of its keys in all
+ * chunks.
+ *
+ *   q            device [Tq, hq, d], dtype                       (read)
+ *   ks, vs       HOST arrays of nchunks device pointers; chunk c's keys and values are
+ *                [Tk_c, hkv, d], dtype, Tk_c = cu_seqlens_k[c * (nseq + 1) + nseq]  (read)
+ *   nchunks      1 .. CPATTN_MAX_CHUNKS
+ *   cu_seqlens_q host int32 [nseq + 1]
+ *   cu_seqlens_k host int32 [nchunks][nseq + 1], row c = chunk c's prefix sums
+ *   q_pos_offset host int32 [nseq] or NULL;  k_pos_offset host int32 [nchunks][nseq] or NULL
+ *   accumulate   0: write (o, lse);  1: fold the share into (o, lse) as cpattn_fwd_chunk_accum
+ *   o, lse       device [Tq, hq, d] / [hq, Tq] fp32 (written; read too if accumulate)
+ *   workspace    device, >= cpattn_workspace_size_chunks(..., nchunks) bytes, 256-byte aligned
+ * The chunks may differ in length per sequence (zero allowed).  o must not
+ * overlap q or any chunk.  Returns CPATTN_OK, or an error code with nothing enqueued.
+ */
+cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void* const* vs,
+                                int32_t nchunks, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const int32_t* q_pos_offset,
+                                const int32_t* k_pos_offset, int32_t nseq, int32_t hq, int32_t hkv,
+                                int32_t d, cpattn_dtype dtype, int32_t causal, int32_t accumulate,
+                                float* o, float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * The online-softmax merge of the pages' ring loop ("Megatron 6D parallelism
  * guide", section 6: m_new = max(m, m_step), alpha = exp(m - m_new),
  * beta = exp(m_step - m_new), l = alpha*l + beta*l_step, O = alpha*O + beta*O_step),
@@ -121,11 +181,14 @@ const char* cpattn_last_error(void);
  * The kernels process "tiles": a run of consecutive query tokens of one
  * sequence, for a group of query heads that share one kv head.  The planner
  * turns host cu_seqlens and position offsets into one entry per (sequence,
- * token block), orders the entries by descending cost (number of key blocks
- * the tile must visit under the causal mask; longest first), and the launch
- * walks them in that order, all head groups of an entry back to back.
+ * token block) and KV chunk, orders the tiles by descending cost (number of key
+ * blocks the tile must visit under the causal mask, summed over the chunks;
+ * longest first), and the launch walks them in that order, all head groups of
+ * a tile back to back.
  *
- * Plan layout: an array of cpattn_plan_entry (32 bytes each).
+ * Plan layout: an array of cpattn_plan_entry (32 bytes each), tile-major: the
+ * entry of tile t and chunk c is at index t * nchunks + c (one entry per tile
+ * for a single chunk).  Entries of one tile share row0, nrows, seq and tblock.
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t row0;     /* first query row (index into Q's T dimension) of the tile */
@@ -139,8 +202,8 @@ typedef struct {
 } cpattn_plan_entry;
 
 typedef struct {
-  int32_t n_entries;        /* (sequence, token block) entries */
-  int32_t n_tiles;          /* work-groups launched = n_entries * head_groups */
+  int32_t n_entries;        /* plan entries = (sequence, token block) tiles x n_chunks */
+  int32_t n_tiles;          /* work-groups launched = n_entries / n_chunks * head_groups */
   int32_t tokens_per_tile;
   int32_t heads_per_tile;
   int32_t head_groups;      /* hq / heads_per_tile */
@@ -148,6 +211,8 @@ typedef struct {
   int64_t visible_pairs;    /* exact visible (query, key) pairs per query head */
   int64_t key_blocks;       /* sum over entries of cost (key blocks visited per head group) */
   size_t plan_bytes;        /* n_entries * sizeof(cpattn_plan_entry) */
+  int32_t n_chunks;         /* KV chunks the plan covers */
+  int32_t reserved;
 } cpattn_plan_info;
 
 /*
@@ -160,6 +225,17 @@ cpattn_status cpattn_plan_build(const int32_t* cu_seqlens_q, const int32_t* cu_s
                                 int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
                                 cpattn_dtype dtype, int32_t causal,
                                 cpattn_plan_entry* plan, size_t plan_bytes, cpattn_plan_info* info);
+
+/*
+ * The plan cpattn_fwd_chunks would launch for nchunks chunks (metadata laid out
+ * as for cpattn_fwd_chunks).  nchunks == 1 gives cpattn_plan_build's plan.
+ */
+cpattn_status cpattn_plan_build_chunks(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                       const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                       int32_t nchunks, int32_t nseq, int32_t hq, int32_t hkv,
+                                       int32_t d, cpattn_dtype dtype, int32_t causal,
+                                       cpattn_plan_entry* plan, size_t plan_bytes,
+                                       cpattn_plan_info* info);
 
 #ifdef __cplusplus
 }

@@ -140,12 +140,13 @@ def test_random_splits_merged_on_gpu_equal_unsplit(gpu_lib, dtype):
             parts_off.append(np.array(offs, np.int32))
         dt = "bfloat16" if dtype == "bf16" else "float32"
         Q = dev(q, dt)
-        o, lse = gpu_lib.cpattn_share(Q, [dev(k[r], dt) for r in parts_rows],
-                                      [dev(v[r], dt) for r in parts_rows], cu_q, parts_cu, qo,
-                                      parts_off, causal=True)
-        torch.cuda.synchronize()
-        check(host(o), host(lse), *attention_ref(q, k, v, cu_q, cu_k, qo, ko, True), dtype,
-              f"split trial {trial} ({n_chunks} chunks)")
+        ref = attention_ref(q, k, v, cu_q, cu_k, qo, ko, True)
+        for mode in gpu_lib.MODES:
+            o, lse = gpu_lib.cpattn_share(Q, [dev(k[r], dt) for r in parts_rows],
+                                          [dev(v[r], dt) for r in parts_rows], cu_q, parts_cu, qo,
+                                          parts_off, causal=True, mode=mode)
+            torch.cuda.synchronize()
+            check(host(o), host(lse), *ref, dtype, f"split trial {trial} ({n_chunks} chunks, {mode})")
 
 
 def test_deterministic(gpu_lib):

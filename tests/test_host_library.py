@@ -180,3 +180,130 @@ def test_merge_rejects_bad_arguments_without_a_gpu(lib):
     assert lib.cpattn_merge(a, la, a, lb, 16, 2, 64, None) == cra._binding.ERR_INVALID_ARG   # alias
     assert lib.cpattn_merge(None, la, b, lb, 16, 2, 64, None) == cra._binding.ERR_INVALID_ARG
     assert lib.cpattn_merge(a, la, b, lb, 0, 2, 64, None) == cra._binding.OK              # empty
+
+
+# ----------------------------------------------------------------------------
+# plans over several KV chunks (cpattn_fwd_chunks)
+# ----------------------------------------------------------------------------
+def _random_split(rng, cu_k, ko, nchunks):
+    """Cut every sequence's keys into nchunks contiguous pieces (empty pieces allowed)."""
+    nseq = len(cu_k) - 1
+    cus, offs = [], []
+    cuts = [sorted(rng.integers(0, cu_k[i + 1] - cu_k[i] + 1, size=nchunks - 1).tolist())
+            for i in range(nseq)]
+    for c in range(nchunks):
+        lens, off = [], []
+        for i in range(nseq):
+            b = [0] + cuts[i] + [int(cu_k[i + 1] - cu_k[i])]
+            lens.append(b[c + 1] - b[c])
+            off.append(int(ko[i]) + b[c])
+        cus.append(wl.cu_from_lengths(lens))
+        offs.append(np.array(off, np.int32))
+    return cus, offs
+
+
+FIELDS = ("row0", "nrows", "k_start", "k_len", "delta", "cost", "seq", "tblock")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [(cra.BF16, 32, 8), (cra.BF16, 8, 1), (cra.FP32, 4, 2)])
+def test_multi_chunk_plan_is_the_per_chunk_plans_tile_major(dtype, hq, hkv):
+    rng = np.random.default_rng(hq + 100 * hkv)
+    for trial in range(20):
+        causal = trial % 4 != 0
+        nseq = int(rng.integers(0, 6))
+        nch = int(rng.integers(1, 9))
+        _, _, _, cu_q, cu_k, qo, ko = wl.random_pack(rng, nseq, 300, 1, 1, 1, dtype="fp32")
+        cus, offs = _random_split(rng, cu_k, ko, nch)
+        ent, info = cra.cpattn_plan_build_chunks(cu_q, cus, qo, offs, hq=hq, hkv=hkv, d=128,
+                                                 dtype=dtype, causal=causal)
+        assert info["n_chunks"] == nch and len(ent) == info["n_entries"]
+        assert len(ent) % nch == 0
+        n_t = len(ent) // nch
+        assert info["n_tiles"] == n_t * hq // info["heads_per_tile"]
+        assert info["visible_pairs"] == sum(visible_pairs_ref(cu_q, cus[c], qo, offs[c], causal)
+                                            for c in range(nch))
+        assert info["key_blocks"] == int(ent["cost"].sum())
+        singles = []
+        for c in range(nch):
+            e1, _ = cra.cpattn_plan_build(cu_q, cus[c], qo, offs[c], hq=hq, hkv=hkv, d=128,
+                                          dtype=dtype, causal=causal)
+            singles.append({(int(e["seq"]), int(e["tblock"])): e for e in e1})
+        tiles = ent.reshape(n_t, nch) if n_t else ent.reshape(0, nch)
+        keys = []
+        for t in range(n_t):
+            key = (int(tiles[t, 0]["seq"]), int(tiles[t, 0]["tblock"]))
+            keys.append(key)
+            for c in range(nch):
+                ref = singles[c][key]
+                assert all(tiles[t, c][f] == ref[f] for f in FIELDS), (t, c)
+        assert len(set(keys)) == n_t and set(keys) == set(singles[0]) if nch else True
+        totals = tiles["cost"].sum(axis=1) if n_t else np.zeros(0)
+        assert np.all(totals[:-1] >= totals[1:])
+        for t in range(n_t - 1):
+            if totals[t] == totals[t + 1]:
+                assert keys[t] < keys[t + 1]
+
+
+def test_one_chunk_plan_equals_plan_build():
+    rng = np.random.default_rng(8)
+    _, _, _, cu_q, cu_k, qo, ko = wl.random_pack(rng, 5, 400, 1, 1, 1, dtype="fp32")
+    a, ia = cra.cpattn_plan_build(cu_q, cu_k, qo, ko, hq=32, hkv=8, d=128)
+    b, ib = cra.cpattn_plan_build_chunks(cu_q, [cu_k], qo, [ko], hq=32, hkv=8, d=128)
+    assert np.array_equal(a, b) and ia == ib
+
+
+def test_workspace_size_chunks_bounds_every_plan():
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        nseq = int(rng.integers(0, 8))
+        cu = wl.cu_from_lengths(rng.integers(0, 500, size=nseq))
+        nch = int(rng.integers(1, 17))
+        for dtype, hq, hkv in [(cra.BF16, 32, 8), (cra.BF16, 8, 8), (cra.FP32, 4, 2)]:
+            _, info = cra.cpattn_plan_build_chunks(cu, [cu] * nch, None, None, hq=hq, hkv=hkv,
+                                                   d=64, dtype=dtype)
+            assert cra.cpattn_workspace_size_chunks(nseq, cu, hq, hkv, 64, nch) >= info["plan_bytes"]
+    cu = wl.cu_from_lengths([10, 20])
+    assert cra.cpattn_workspace_size_chunks(2, cu, 4, 2, 64, 0) == 0
+    assert cra.cpattn_workspace_size_chunks(2, cu, 4, 2, 64, cra.MAX_CHUNKS + 1) == 0
+    assert cra.cpattn_workspace_size_chunks(2, cu, 4, 2, 64, 1) == cra.cpattn_workspace_size(2, cu, 4, 2, 64)
+
+
+def test_plan_build_chunks_rejects_bad_chunk_counts(lib):
+    cu, pcu = _i32([0, 5])
+    info = cra._binding.PlanInfo()
+    for nch in (0, -1, cra.MAX_CHUNKS + 1):
+        st = lib.cpattn_plan_build_chunks(pcu, pcu, None, None, nch, 1, 4, 2, 64, 0, 1, None, 0,
+                                          ctypes.byref(info))
+        assert st == cra._binding.ERR_INVALID_ARG
+    bad, pbad = _i32([0, 5, 0, -3])  # second chunk's prefix sums decrease
+    st = lib.cpattn_plan_build_chunks(pcu, pbad, None, None, 2, 1, 4, 2, 64, 0, 1, None, 0,
+                                      ctypes.byref(info))
+    assert st == cra._binding.ERR_INVALID_ARG
+    bad, pbad = _i32([0, 5, 1, 4])   # second chunk does not start at 0
+    st = lib.cpattn_plan_build_chunks(pcu, pbad, None, None, 2, 1, 4, 2, 64, 0, 1, None, 0,
+                                      ctypes.byref(info))
+    assert st == cra._binding.ERR_INVALID_ARG and b"chunk 1" in lib.cpattn_last_error()
+
+
+def test_fwd_chunks_rejects_bad_arguments_without_a_gpu(lib):
+    cu, pcu = _i32([0, 64])
+    cu2, pcu2 = _i32([0, 64, 0, 64])
+    fake = ctypes.c_void_p(4096)
+    ptrs = lambda *a: (ctypes.c_void_p * len(a))(*a)
+    ks, vs = ptrs(1 << 24, 1 << 25), ptrs(1 << 26, 1 << 27)
+    ws = ctypes.c_void_p(1 << 20)
+
+    def call(**kw):
+        return lib.cpattn_fwd_chunks(
+            kw.get("q", fake), kw.get("ks", ks), kw.get("vs", vs), kw.get("nch", 2), pcu,
+            kw.get("cuk", pcu2), None, None, 1, 4, 2, 64, kw.get("dtype", 0), 1, kw.get("acc", 0),
+            kw.get("o", ctypes.c_void_p(1 << 30)), ctypes.c_void_p(1 << 31), ws, 1 << 20, None)
+
+    assert call(nch=0) == cra._binding.ERR_INVALID_ARG
+    assert call(nch=cra.MAX_CHUNKS + 1) == cra._binding.ERR_INVALID_ARG
+    assert call(ks=None) == cra._binding.ERR_INVALID_ARG
+    assert call(acc=2) == cra._binding.ERR_INVALID_ARG
+    assert call(ks=ptrs(1 << 24, (1 << 25) + 8)) == cra._binding.ERR_INVALID_ARG     # misaligned k
+    assert call(vs=ptrs(1 << 26, None)) == cra._binding.ERR_INVALID_ARG             # null v
+    assert call(o=ctypes.c_void_p(1 << 25)) == cra._binding.ERR_INVALID_ARG         # o overlaps chunk 1's k
+    assert b"overlap" in lib.cpattn_last_error()

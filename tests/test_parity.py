@@ -5,8 +5,10 @@ sequence (all rows), the 4,096-token pack (all rows), and at full size the
 CP4 share of a 16,384-token budget, the 128K-context CP=4 share and the
 dynamic-CP mixed pack (sampled rows, always including every sequence's first
 and last rows and tile boundaries).  Each chunk's partial is checked against
-the oracle's attention over that chunk, and the merged share against the
-oracle's unsplit attention over all of the sequence's keys.
+the oracle's attention over that chunk, and the share -- in each of its three
+schedules: one launch over all chunks, per-chunk launches accumulating in the
+epilogue, per-chunk partials merged by the merge kernel -- against the oracle's
+unsplit attention over all of the sequence's keys.
 """
 import numpy as np
 import pytest
@@ -18,14 +20,14 @@ from parity_util import check, dev, dtype_name, host, sample_rows
 pytestmark = pytest.mark.gpu
 
 
-def _run_group(cra, w, g, rows=None):
+def _run_group(cra, w, g, rows=None, mode="stream"):
     import torch
     dt = dtype_name(w.dtype)
     q = dev(g.q, dt)
     ks = [dev(c.k, dt) for c in g.chunks]
     vs = [dev(c.v, dt) for c in g.chunks]
     o, lse = cra.cpattn_share(q, ks, vs, g.cu_q, [c.cu_k for c in g.chunks], g.q_off,
-                              [c.k_off for c in g.chunks], causal=w.causal)
+                              [c.k_off for c in g.chunks], causal=w.causal, mode=mode)
     torch.cuda.synchronize()
     o_h, l_h = host(o), host(lse)
     if rows is not None:
@@ -33,11 +35,20 @@ def _run_group(cra, w, g, rows=None):
     return q, ks, vs, o_h, l_h
 
 
+def _all_modes(cra, w, g, ref, rows=None, what=""):
+    """Every schedule of the share (one launch over all chunks, epilogue accumulation,
+    explicit partials + merge) against the same oracle result."""
+    out = None
+    for mode in cra.MODES:
+        out = _run_group(cra, w, g, rows, mode)
+        check(out[3], out[4], *ref, w.dtype if w.dtype == "bf16" else "fp32", f"{what} [{mode}]")
+    return out
+
+
 def test_tiny_fp32_share_and_chunks(gpu_lib):
     w = wl.make("tiny", 0)
     g = w.groups[0]
-    q, ks, vs, o, lse = _run_group(gpu_lib, w, g)
-    check(o, lse, *share_ref(g), "fp32", "tiny share")
+    q, ks, vs, o, lse = _all_modes(gpu_lib, w, g, share_ref(g), what="tiny share")
     for c, ch in enumerate(g.chunks):
         oc, lc = gpu_lib.cpattn_fwd_chunk(q, ks[c], vs[c], g.cu_q, ch.cu_k, g.q_off, ch.k_off)
         check(host(oc), host(lc), *attention_ref(g.q, ch.k, ch.v, g.cu_q, ch.cu_k, g.q_off, ch.k_off),
@@ -48,8 +59,7 @@ def test_tiny_fp32_share_and_chunks(gpu_lib):
 def test_pack_bf16_all_rows(gpu_lib, seed):
     w = wl.make("pack", seed)
     g = w.groups[0]
-    _, _, _, o, lse = _run_group(gpu_lib, w, g)
-    check(o, lse, *share_ref(g), "bf16", f"pack seed {seed}")
+    _all_modes(gpu_lib, w, g, share_ref(g), what=f"pack seed {seed}")
 
 
 def test_cp4_share_full_size(gpu_lib):
@@ -57,8 +67,7 @@ def test_cp4_share_full_size(gpu_lib):
     w = wl.make("cp4_share", 0)
     g = w.groups[0]
     rows = sample_rows(g.cu_q, 32, extra=256)
-    q, ks, vs, o, lse = _run_group(gpu_lib, w, g, rows)
-    check(o, lse, *share_ref(g, rows=rows), "bf16", "cp4 share")
+    q, ks, vs, o, lse = _all_modes(gpu_lib, w, g, share_ref(g, rows=rows), rows, "cp4 share")
     for c, ch in enumerate(g.chunks):
         oc, lc = gpu_lib.cpattn_fwd_chunk(q, ks[c], vs[c], g.cu_q, ch.cu_k, g.q_off, ch.k_off)
         ref = attention_ref(g.q, ch.k, ch.v, g.cu_q, ch.cu_k, g.q_off, ch.k_off, rows=rows)
@@ -69,16 +78,14 @@ def test_ctx128k_share_full_size(gpu_lib):
     w = wl.make("ctx128k_share", 0)
     g = w.groups[0]
     rows = sample_rows(g.cu_q, 2048, extra=96)
-    _, _, _, o, lse = _run_group(gpu_lib, w, g, rows)
-    check(o, lse, *share_ref(g, rows=rows), "bf16", "128k share")
+    _all_modes(gpu_lib, w, g, share_ref(g, rows=rows), rows, "128k share")
 
 
 def test_dcp_mixed_full_size(gpu_lib):
     w = wl.make("dcp_mixed", 0)
     for gi, g in enumerate(w.groups):
         rows = sample_rows(g.cu_q, 512, extra=64, seed=gi)
-        _, _, _, o, lse = _run_group(gpu_lib, w, g, rows)
-        check(o, lse, *share_ref(g, rows=rows), "bf16", f"dcp group cp={len(g.chunks)}")
+        _all_modes(gpu_lib, w, g, share_ref(g, rows=rows), rows, f"dcp group cp={len(g.chunks)}")
 
 
 def test_merge_matches_oracle_and_is_exact_for_empty_sides(gpu_lib):
