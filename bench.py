@@ -31,11 +31,11 @@ METRIC = "causal attn TFLOP/s + MFMA util%, 16K-token THD pack at CP4-share, 1 G
 BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 ATTN_SOURCE = os.path.join(HERE, "context_ring_attention_amd", "csrc", "attn_fwd_bf16.hip")
-# HBM bytes per attention launch on this workload, from rocprofv3 FETCH_SIZE and WRITE_SIZE
-# runs (scaled by a plain-copy calibration), keyed by the sha256 of the kernel source they
-# were taken on.  Any other source reports traffic as null until it is profiled again.
+# HBM bytes per streaming attention launch, from rocprofv3 FETCH_SIZE and WRITE_SIZE runs
+# (scaled by a plain-copy calibration), keyed by workload and the sha256 of the kernel source
+# they were taken on.  Any other pair reports traffic as null until it is profiled again.
 PROFILED_TRAFFIC = {
-    "39c909d6413ed85e8132368b88218206724352465a99ffbfe784ecd66b444c8b": 132298236,
+    ("cp4_share", "2b8e1b79d16083ab3b7717095bb764caf95067a5e79bf8180c95ba3317755a9f"): 225710736,
 }
 
 
@@ -83,6 +83,9 @@ def main() -> int:
     ap.add_argument("--workload", default="cp4_share")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedules", default="merge,accum,stream",
+                    help="comma-separated schedules to time besides the step itself (stream is "
+                         "always timed, last)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain elementwise copy of MIB MiB "
                          "(reference point for HBM byte counters)")
@@ -171,8 +174,13 @@ def main() -> int:
             gc.unfreeze()
         return t_start.elapsed_time(t_end) / args.steps
 
+    wanted = [m for m in args.schedules.split(",") if m]
+    if any(m not in cra.MODES for m in wanted):
+        print(f"--schedules takes names from {cra.MODES}", file=sys.stderr)
+        return 2
+    order = [m for m in ("merge", "accum") if m in wanted] + ["stream"]
     schedules = {}
-    for mode in ("merge", "accum", "stream"):   # the headline schedule last, on a warm GPU
+    for mode in order:   # the step's own schedule last, on a warm GPU
         ms = timed(mode)
         launches = 1 if mode == "stream" else nch
         a_ms = sum(row[c][0].elapsed_time(row[c][1]) for row in attn_ev[mode]
@@ -187,13 +195,14 @@ def main() -> int:
     attn_avg_ms = schedules["stream"]["attn_avg_launch_us"] / 1e3
     attn_flops_per_launch = flops_step
     attn_tflops = attn_flops_per_launch / (attn_avg_ms / 1e3) / 1e12
-    merge_ms = sum(a.elapsed_time(b) for row in merge_ev for a, b in row)
+    timed_merge = "merge" in schedules and n_merge > 0
+    merge_ms = sum(a.elapsed_time(b) for row in merge_ev for a, b in row) if timed_merge else 0.0
     merge_avg_ms = merge_ms / max(1, args.steps * n_merge)
-    merge_gbs = merge_bytes / (merge_avg_ms / 1e3) / 1e9 if n_merge else None
+    merge_gbs = merge_bytes / (merge_avg_ms / 1e3) / 1e9 if timed_merge else None
 
     import hashlib
     with open(ATTN_SOURCE, "rb") as f:
-        traffic = PROFILED_TRAFFIC.get(hashlib.sha256(f.read()).hexdigest())
+        traffic = PROFILED_TRAFFIC.get((args.workload, hashlib.sha256(f.read()).hexdigest()))
     tk_all = sum(int(c[-1]) for c in cu_ks)
     attn_bytes = tq * w.hq * w.d * 2 + 2 * tk_all * w.hkv * w.d * 2 + tq * w.hq * w.d * 4 + tq * w.hq * 4
     result = {
@@ -225,7 +234,7 @@ def main() -> int:
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
                      "flops_per_launch": attn_flops_per_launch},
         "schedules": schedules,
-        "merge": {"schedule": "merge", "avg_launch_us": round(merge_avg_ms * 1e3, 2) if n_merge else None,
+        "merge": {"schedule": "merge", "avg_launch_us": round(merge_avg_ms * 1e3, 2) if timed_merge else None,
                   "bytes_per_launch": merge_bytes, "achieved_GBs": round(merge_gbs, 1) if merge_gbs else None,
                   "hbm_frac": round(merge_gbs / HBM_PEAK_GBS, 4) if merge_gbs else None},
         "flops_per_step": flops_step,

@@ -43,7 +43,17 @@
 // of the accumulator on almost every block.
 //
 // Row sums are taken on the bf16-rounded P with v_dot2_f32_bf16 (two keys per
-// instruction), so l sums exactly the weights the PV product multiplies.
+// instruction), so l sums exactly the weights the PV product multiplies.  Most
+// blocks skip the row max altogether: once a reference max is set, P is formed
+// against it directly, and a lane sum <= 2^8 proves no score passed the
+// threshold (every p >= 0), which is all the max was needed for; otherwise the
+// block is redone with the max (and rescale) first.  Both paths give the same
+// bits as always taking the max.
+//
+// Scheduling: the two waves of a SIMD (one from each of the CU's two
+// work-groups) run the same block loop; a wave raises its issue priority for
+// its matrix-core runs (scores, PV) and drops it for the softmax, so when the
+// two meet, the MFMA stream is the one that keeps issuing.
 //
 // Masking: the host classifies blocks by global position, so only blocks on the
 // causal diagonal or past the sequence end pay for per-element masking.  A row
@@ -232,6 +242,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         const char* s = smem + stage * L::kStage;
         // ---- S^T = K Q^T for 64 keys (two 32-key tiles) ----
         // K fragments are read one k-step ahead of the MFMAs that consume them.
+        __builtin_amdgcn_s_setprio(1);
         f32x16 s0 = f32x16{}, s1 = f32x16{};
         bf16x8 a0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][0]);
         bf16x8 a1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][0]);
@@ -249,6 +260,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
             a1 = n1;
           }
         }
+        __builtin_amdgcn_s_setprio(0);
         // ---- mask (diagonal / ragged blocks only) ----
         if (j >= nfull_w) {
           // key (within block) of register r: 32 kt + 8 (r / 4) + 4 g + r % 4
@@ -261,42 +273,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
           }
         }
         // ---- online softmax ----
-        float mx;
-        {
-          float t[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) t[r] = __builtin_elementwise_max(s0[r], s1[r]);
-#pragma unroll
-          for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-            for (int r = 0; r < w; ++r) t[r] = __builtin_elementwise_max(t[r], t[r + w]);
-          mx = pair_max(t[0]);
-        }
-        if (__any(mx > m_run + thr)) {
-          const float m_new = __builtin_elementwise_max(m_run, mx);
-          const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-          const float alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * scale_log2);
-#pragma unroll
-          for (int i = 0; i < DT; ++i) acc[i] *= alpha;
-          l_run *= alpha;
-          m_run = m_new;
-        }
-        const float neg = -((m_run == -INFINITY) ? 0.f : m_run) * scale_log2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, neg));
-          s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, neg));
-        }
-        // P as bf16 B operands: key group kk takes registers 8 (kk % 2) .. +7 of tile kk / 2
+        // P = exp2(s c - m c) as bf16 B operands (key group kk = registers 8 (kk % 2) .. +7 of
+        // tile kk / 2) and this lane's sum of them.
         bf16x8 pf[4];
+        auto exp_block = [&](float neg) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          pf[0][jj] = (__bf16)s0[jj];
-          pf[1][jj] = (__bf16)s0[8 + jj];
-          pf[2][jj] = (__bf16)s1[jj];
-          pf[3][jj] = (__bf16)s1[8 + jj];
-        }
-        {
+          for (int jj = 0; jj < 8; ++jj) {
+            pf[0][jj] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[jj], scale_log2, neg));
+            pf[1][jj] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[8 + jj], scale_log2, neg));
+            pf[2][jj] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[jj], scale_log2, neg));
+            pf[3][jj] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[8 + jj], scale_log2, neg));
+          }
           const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
           float part[4];
 #pragma unroll
@@ -307,9 +294,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
               part[kk] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[kk][2 * i], pf[kk][2 * i + 1]},
                                                          ones, part[kk], false);
           }
-          l_run += (part[0] + part[1]) + (part[2] + part[3]);
+          return (part[0] + part[1]) + (part[2] + part[3]);
+        };
+        // Fast path: with a reference max already set, a lane sum <= 2^8 proves every p of the
+        // lane <= 2^8, i.e. no score passed the rescale threshold: the block needs no max.
+        bool slow = __any(m_run == -INFINITY);
+        float lane_sum = 0.f;
+        if (!slow) {
+          lane_sum = exp_block(-m_run * scale_log2);
+          slow = __any(!(lane_sum <= 256.0f));
         }
+        if (slow) {
+          float mx;
+          {
+            float t[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) t[r] = __builtin_elementwise_max(s0[r], s1[r]);
+#pragma unroll
+            for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+              for (int r = 0; r < w; ++r) t[r] = __builtin_elementwise_max(t[r], t[r + w]);
+            mx = pair_max(t[0]);
+          }
+          if (__any(mx > m_run + thr)) {
+            const float m_new = __builtin_elementwise_max(m_run, mx);
+            const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * scale_log2);
+#pragma unroll
+            for (int i = 0; i < DT; ++i) acc[i] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
+          }
+          lane_sum = exp_block(-((m_run == -INFINITY) ? 0.f : m_run) * scale_log2);
+        }
+        l_run += lane_sum;
         // ---- O^T += V^T P^T ----
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int row = 16 * kk + 4 * g + jr;
@@ -324,6 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], acc[dt], 0, 0, 0);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     c = cn;
