@@ -32,7 +32,13 @@ blocks only to bound memory.  It is not an online softmax and never splits a
 row's keys, so it shares neither code nor algorithm with the GPU kernels.
 
 merge_ref follows the pages' merge steps in their own notation (m_new, alpha,
-beta, l, O).  Every function here is pinned by tests/test_oracle.py (brute force,
+beta, l, O).
+
+attention_bwd_ref is the gradient of the same function.  The pages train with
+context parallelism (a forward-backward pass per micro-batch); they print no
+backward of the attention, and the reading taken is the plain one: the gradient
+of O = softmax(Q K^T / sqrt(D) + mask) V with respect to Q, K and V for an
+upstream gradient dO, written out by the chain rule through the row softmax.  Every function here is pinned by tests/test_oracle.py (brute force,
 closed forms, torch's scaled_dot_product_attention, invariants); none is
 "parity unpinned".
 """
@@ -43,7 +49,8 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["attention_ref", "merge_ref", "share_ref", "visible_pairs_ref", "flops_ref"]
+__all__ = ["attention_ref", "attention_bwd_ref", "merge_ref", "share_ref", "share_bwd_ref",
+           "visible_pairs_ref", "flops_ref"]
 
 _ROW_BLOCK = 256
 
@@ -114,6 +121,63 @@ def attention_ref(q, k, v, cu_q, cu_k, q_off=None, k_off=None, causal: bool = Tr
     return o, lse
 
 
+def attention_bwd_ref(q, k, v, do, cu_q, cu_k, q_off=None, k_off=None,
+                      causal: bool = True) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of attention_ref's O with respect to q, k, v for upstream gradient do (fp64).
+
+    Per packed sequence and query head h (kv head g), with S = Q K_g^T / sqrt(D) masked as
+    in attention_ref and P its row softmax (rows with no visible key have P = 0):
+        dV_g += P^T dO                          (O = P V)
+        dP    = dO V_g^T
+        dS    = P * (dP - rowsum(P * dP))       (Jacobian of the row softmax)
+        dQ_h  = dS K_g / sqrt(D)
+        dK_g += dS^T Q_h / sqrt(D)
+    A kv head's gradient sums the contributions of every query head of its group.
+    Rows are processed in blocks, each row against all its keys (a row's softmax is never
+    split).  Returns dq [Tq, Hq, D], dk and dv [Tk, Hkv, D] (float64).
+    """
+    q = np.asarray(q); k = np.asarray(k); v = np.asarray(v); do = np.asarray(do)
+    cu_q = np.asarray(cu_q, dtype=np.int64); cu_k = np.asarray(cu_k, dtype=np.int64)
+    nseq = len(cu_q) - 1
+    q_off = np.zeros(nseq, np.int64) if q_off is None else np.asarray(q_off, dtype=np.int64)
+    k_off = np.zeros(nseq, np.int64) if k_off is None else np.asarray(k_off, dtype=np.int64)
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    assert hq % hkv == 0, "query heads must be a multiple of kv heads"
+    scale = 1.0 / math.sqrt(d)
+    dq = np.zeros((tq, hq, d), dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for i in range(nseq):
+        k_i = _as64(k[cu_k[i]:cu_k[i + 1]])
+        v_i = _as64(v[cu_k[i]:cu_k[i + 1]])
+        nk = k_i.shape[0]
+        u = np.arange(nk)
+        for t0 in range(int(cu_q[i]), int(cu_q[i + 1]), _ROW_BLOCK):
+            t1 = min(t0 + _ROW_BLOCK, int(cu_q[i + 1]))
+            bt = np.arange(t0, t1) - cu_q[i]
+            if causal:
+                vis = (k_off[i] + u[None, :]) <= (q_off[i] + bt[:, None])
+            else:
+                vis = np.ones((bt.size, nk), dtype=bool)
+            nonempty = vis.any(axis=1)
+            for h in range(hq):
+                g = (h * hkv) // hq
+                qb = _as64(q[t0:t1, h])
+                dob = _as64(do[t0:t1, h])
+                s = np.where(vis, (qb @ k_i[:, g].T) * scale, -np.inf)
+                m = np.where(nonempty, np.max(s, axis=1, initial=-np.inf), 0.0)
+                e = np.exp(s - m[:, None])
+                l = np.where(nonempty, e.sum(axis=1), 1.0)
+                p = e / l[:, None]                                  # 0 on hidden keys and empty rows
+                dv[cu_k[i]:cu_k[i + 1], g] += p.T @ dob
+                dp = dob @ v_i[:, g].T
+                ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+                dq[t0:t1, h] = (ds @ k_i[:, g]) * scale
+                dk[cu_k[i]:cu_k[i + 1], g] += (ds.T @ qb) * scale
+    return dq, dk, dv
+
+
 def merge_ref(o_a, lse_a, o_b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
     """Merge two partial results over disjoint key sets (fp64).
 
@@ -148,6 +212,15 @@ def share_ref(group, causal: bool = True, rows=None) -> Tuple[np.ndarray, np.nda
     nseq = len(group.cu_q) - 1
     return attention_ref(group.q, group.k_full, group.v_full, group.cu_q, group.cu_full,
                          group.q_off, np.zeros(nseq, np.int64), causal=causal, rows=rows)
+
+
+def share_bwd_ref(group, do, causal: bool = True) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of a rank's whole share (its Q against every key of its sequences) for the
+    upstream gradient do [Tq, Hq, D]: dq [Tq, Hq, D] and dk, dv over the whole sequences'
+    keys [Tfull, Hkv, D] (rows of k_full / v_full)."""
+    nseq = len(group.cu_q) - 1
+    return attention_bwd_ref(group.q, group.k_full, group.v_full, do, group.cu_q, group.cu_full,
+                             group.q_off, np.zeros(nseq, np.int64), causal=causal)
 
 
 def visible_pairs_ref(cu_q, cu_k, q_off=None, k_off=None, causal: bool = True) -> int:

@@ -361,3 +361,105 @@ def test_visible_pairs_by_brute_enumeration():
     # a causal diagonal block of n tokens holds n(n+1)/2 pairs
     assert visible_pairs_ref([0, 100], [0, 100]) == 100 * 101 // 2
     assert flops_ref(32896, 2, 64) == 16_842_752          # tiny workload: 16.84 MFLOP
+
+
+# ----------------------------------------------------------------------------
+# backward: gradients of the same function
+# ----------------------------------------------------------------------------
+from oracle import attention_bwd_ref  # noqa: E402
+
+
+@pytest.mark.parametrize("seed,hq,hkv,d,causal", [(0, 4, 2, 16, True), (1, 8, 1, 32, True),
+                                                   (2, 2, 2, 8, False), (3, 6, 3, 4, True)])
+def test_bwd_matches_torch_autograd(seed, hq, hkv, d, causal):
+    """torch autograd through scaled_dot_product_attention (float64, explicit mask, its own
+    GQA grouping) gives the same dq, dk, dv."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    q, k, v, cu_q, cu_k, qo, ko = _rand_pack(seed, 3, 40, hq, hkv, d, min_len=1)
+    ko = np.minimum(ko, qo)           # every query sees at least the sequence's first key
+    do = np.random.default_rng(seed + 50).standard_normal(q.shape)
+    dq_ref, dk_ref, dv_ref = attention_bwd_ref(q, k, v, do, cu_q, cu_k, qo, ko, causal)
+    for i in range(3):
+        qs = torch.tensor(np.asarray(q[cu_q[i]:cu_q[i + 1]], np.float64).transpose(1, 0, 2),
+                          requires_grad=True)
+        ks = torch.tensor(np.asarray(k[cu_k[i]:cu_k[i + 1]], np.float64).transpose(1, 0, 2),
+                          requires_grad=True)
+        vs = torch.tensor(np.asarray(v[cu_k[i]:cu_k[i + 1]], np.float64).transpose(1, 0, 2),
+                          requires_grad=True)
+        nq, nk = qs.shape[1], ks.shape[1]
+        if causal:
+            mask = (int(ko[i]) + torch.arange(nk))[None, :] <= (int(qo[i]) + torch.arange(nq))[:, None]
+        else:
+            mask = torch.ones(nq, nk, dtype=torch.bool)
+        out = F.scaled_dot_product_attention(qs, ks, vs, attn_mask=mask, enable_gqa=True)
+        dos = torch.tensor(np.asarray(do[cu_q[i]:cu_q[i + 1]]).transpose(1, 0, 2))
+        (out * dos).sum().backward()
+        np.testing.assert_allclose(dq_ref[cu_q[i]:cu_q[i + 1]], qs.grad.numpy().transpose(1, 0, 2),
+                                   atol=1e-11)
+        np.testing.assert_allclose(dk_ref[cu_k[i]:cu_k[i + 1]], ks.grad.numpy().transpose(1, 0, 2),
+                                   atol=1e-11)
+        np.testing.assert_allclose(dv_ref[cu_k[i]:cu_k[i + 1]], vs.grad.numpy().transpose(1, 0, 2),
+                                   atol=1e-11)
+
+
+def test_bwd_central_differences():
+    """Each gradient entry against (L(x + e) - L(x - e)) / 2e of L = sum(O * dO), with O from
+    the pinned forward, on a tiny pack with an empty row and a causal diagonal."""
+    rng = np.random.default_rng(7)
+    cu_q, cu_k = np.array([0, 3, 5]), np.array([0, 4, 7])
+    qo, ko = np.array([1, 0]), np.array([0, 1])          # row 0 of sequence 1 sees no key
+    hq, hkv, d = 2, 1, 3
+    q = rng.standard_normal((5, hq, d)); k = rng.standard_normal((7, hkv, d))
+    v = rng.standard_normal((7, hkv, d)); do = rng.standard_normal((5, hq, d))
+    dq, dk, dv = attention_bwd_ref(q, k, v, do, cu_q, cu_k, qo, ko, True)
+
+    def loss(q_, k_, v_):
+        o, _ = attention_ref(q_, k_, v_, cu_q, cu_k, qo, ko, True)
+        return float(np.sum(o * do))
+
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            args = {"q": (q, k, v), "k": (q, k, v), "v": (q, k, v)}[name]
+            ap = [a.copy() for a in args]; am = [a.copy() for a in args]
+            pos = "qkv".index(name)
+            ap[pos] = xp; am[pos] = xm
+            num[idx] = (loss(*ap) - loss(*am)) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=1e-7, err_msg=name)
+    assert np.all(dq[3] == 0.0)                         # the empty row has no gradient
+
+
+def test_bwd_closed_forms():
+    rng = np.random.default_rng(8)
+    # one key per sequence: P = 1 for every row that sees it -> dq = dk = 0, dv = sum of dO
+    cu_q, cu_k = np.array([0, 4]), np.array([0, 1])
+    q = rng.standard_normal((4, 2, 8)); k = rng.standard_normal((1, 1, 8))
+    v = rng.standard_normal((1, 1, 8)); do = rng.standard_normal((4, 2, 8))
+    dq, dk, dv = attention_bwd_ref(q, k, v, do, cu_q, cu_k, None, None, True)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_allclose(dv[0, 0], do.sum(axis=(0, 1)), atol=1e-12)
+    # identical value rows: O does not depend on the weights -> dq = dk = 0, dv = P^T dO
+    cu_q, cu_k = np.array([0, 6]), np.array([0, 9])
+    q = rng.standard_normal((6, 1, 4)); k = rng.standard_normal((9, 1, 4))
+    v = np.tile(rng.standard_normal((1, 1, 4)), (9, 1, 1)); do = rng.standard_normal((6, 1, 4))
+    dq, dk, dv = attention_bwd_ref(q, k, v, do, cu_q, cu_k, [3], [0], True)
+    assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
+    # the total dv is the total dO whatever the weights (every row's P sums to 1)
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
+
+
+def test_bwd_gqa_equals_summed_mha():
+    """A kv head's gradient is the sum over its query group of the MHA gradients with the kv
+    head repeated."""
+    q, k, v, cu_q, cu_k, qo, ko = _rand_pack(21, 3, 30, 6, 2, 8, min_len=1)
+    do = np.random.default_rng(22).standard_normal(q.shape)
+    dq, dk, dv = attention_bwd_ref(q, k, v, do, cu_q, cu_k, qo, ko, True)
+    k_rep = np.repeat(k, 3, axis=1); v_rep = np.repeat(v, 3, axis=1)
+    dq_m, dk_m, dv_m = attention_bwd_ref(q, k_rep, v_rep, do, cu_q, cu_k, qo, ko, True)
+    _close(dq, dq_m, 1e-12)
+    _close(dk, dk_m.reshape(dk.shape[0], 2, 3, 8).sum(axis=2), 1e-12)
+    _close(dv, dv_m.reshape(dv.shape[0], 2, 3, 8).sum(axis=2), 1e-12)
