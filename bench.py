@@ -86,6 +86,8 @@ def main() -> int:
     ap.add_argument("--schedules", default="merge,accum,stream",
                     help="comma-separated schedules to time besides the step itself (stream is "
                          "always timed, last)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward of the share (reported under 'backward')")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain elementwise copy of MIB MiB "
                          "(reference point for HBM byte counters)")
@@ -200,6 +202,54 @@ def main() -> int:
     merge_avg_ms = merge_ms / max(1, args.steps * n_merge)
     merge_gbs = merge_bytes / (merge_avg_ms / 1e3) / 1e9 if timed_merge else None
 
+    backward = None
+    if not args.no_backward:
+        # Backward of the share: for each chunk, cpattn_bwd_chunk adds its dq contribution and
+        # yields the chunk's dk, dv, from the share's forward (o, lse) and a synthetic gradient.
+        o_f, lse_f = bufs.o_acc, bufs.lse_acc
+        cra.cpattn_fwd_chunks(q, ks, vs, cu_q, cu_ks, q_off, k_offs, True, out=o_f, lse=lse_f,
+                              workspace=bufs.workspace, stream=stream)
+        gen = torch.Generator(device="cuda").manual_seed(args.seed + 1)
+        dout = torch.randn(q.shape, device="cuda", generator=gen).to(bf)
+        f32 = dict(dtype=torch.float32, device="cuda")
+        dq = torch.zeros(q.shape, **f32)
+        dks = [torch.zeros(k.shape, **f32) for k in ks]
+        dvs = [torch.zeros(v.shape, **f32) for v in vs]
+        bws = torch.empty(max(cra.cpattn_bwd_workspace_size(len(cu_q) - 1, cu_q, cu_ks[0], w.hq,
+                                                            w.hkv, w.d), 256),
+                          dtype=torch.uint8, device="cuda")
+
+        def bwd_step():
+            for c in range(nch):
+                cra.cpattn_bwd_chunk(q, ks[c], vs[c], o_f, lse_f, dout, cu_q, cu_ks[c], q_off,
+                                     k_offs[c], True, dq=dq, dk=dks[c], dv=dvs[c], workspace=bws,
+                                     stream=stream)
+
+        for _ in range(max(1, args.warmup)):
+            bwd_step()
+        torch.cuda.synchronize()
+        gc.collect()
+        gc.freeze()
+        gc.disable()
+        try:
+            b0, b1 = ev(), ev()
+            b0.record(stream)
+            for _ in range(args.steps):
+                bwd_step()
+            b1.record(stream)
+            torch.cuda.synchronize()
+        finally:
+            gc.enable()
+            gc.unfreeze()
+        bwd_ms = b0.elapsed_time(b1) / args.steps
+        bwd_flops = 10 * w.d * w.hq * sum(pairs_chunk)
+        backward = {"ms_per_step": round(bwd_ms, 4),
+                    "tflops": round(bwd_flops / (bwd_ms / 1e3) / 1e12, 2),
+                    "frac": round(bwd_flops / (bwd_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "flops_per_step": bwd_flops,
+                    "counted_as": "10 D Hq per visible pair (5 products of the forward's 2 D Hq)",
+                    "launches_per_step": f"{nch} x (delta, dQ, dK/dV)"}
+
     import hashlib
     with open(ATTN_SOURCE, "rb") as f:
         traffic = PROFILED_TRAFFIC.get((args.workload, hashlib.sha256(f.read()).hexdigest()))
@@ -234,6 +284,7 @@ def main() -> int:
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
                      "flops_per_launch": attn_flops_per_launch},
         "schedules": schedules,
+        "backward": backward,
         "merge": {"schedule": "merge", "avg_launch_us": round(merge_avg_ms * 1e3, 2) if timed_merge else None,
                   "bytes_per_launch": merge_bytes, "achieved_GBs": round(merge_gbs, 1) if merge_gbs else None,
                   "hbm_frac": round(merge_gbs / HBM_PEAK_GBS, 4) if merge_gbs else None},

@@ -23,7 +23,8 @@ BF16, FP32 = 0, 1
 
 # Every symbol include/cpattn.h declares.
 EXPORTED = ("cpattn_workspace_size", "cpattn_workspace_size_chunks", "cpattn_fwd_chunk",
-            "cpattn_fwd_chunk_accum", "cpattn_fwd_chunks", "cpattn_merge", "cpattn_status_string",
+            "cpattn_fwd_chunk_accum", "cpattn_fwd_chunks", "cpattn_bwd_chunk",
+            "cpattn_bwd_workspace_size", "cpattn_merge", "cpattn_status_string",
             "cpattn_last_error", "cpattn_plan_build", "cpattn_plan_build_chunks")
 MAX_CHUNKS = 16  # CPATTN_MAX_CHUNKS
 
@@ -75,6 +76,13 @@ def load(path: str = LIB_PATH):
                                       _I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
                                       c_int32, c_int, c_int32, c_int32, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]
+    lib.cpattn_bwd_chunk.restype = c_int
+    lib.cpattn_bwd_chunk.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     _I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
+                                     c_int32, c_int, c_int32, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]
+    lib.cpattn_bwd_workspace_size.restype = c_size_t
+    lib.cpattn_bwd_workspace_size.argtypes = [c_int32, _I32P, _I32P, c_int32, c_int32, c_int32]
     lib.cpattn_merge.restype = c_int
     lib.cpattn_merge.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32,
                                  c_void_p]
@@ -323,6 +331,67 @@ def cpattn_fwd_chunks(q, ks: Sequence, vs: Sequence, cu_seqlens_q, cu_seqlens_ks
                                  c_void_p(workspace.data_ptr()), workspace.numel(),
                                  _stream_handle(stream)))
     return out, lse
+
+
+def cpattn_bwd_workspace_size(nseq: int, cu_seqlens_q, cu_seqlens_k, hq: int, hkv: int,
+                              d: int) -> int:
+    cq, pq = _host_i32(cu_seqlens_q, nseq + 1, "cu_seqlens_q")
+    ck, pk = _host_i32(cu_seqlens_k, nseq + 1, "cu_seqlens_k")
+    return int(load().cpattn_bwd_workspace_size(nseq, pq, pk, hq, hkv, d))
+
+
+def cpattn_bwd_chunk(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, q_pos_offset=None,
+                     k_pos_offset=None, causal: bool = True, dq=None, dk=None, dv=None,
+                     workspace=None, stream=None):
+    """Backward of one KV chunk: ADDS this chunk's contributions to dq, dk, dv (fp32 CUDA
+    tensors, zero-filled when not given) and returns (dq, dk, dv).
+
+    q, do [Tq, Hq, D] and k, v [Tk, Hkv, D]: bfloat16; o [Tq, Hq, D] and lse [Hq, Tq]: the
+    share's final forward output (float32).
+    """
+    import torch
+    lib = load()
+    cq, pq = _host_i32(cu_seqlens_q, None, "cu_seqlens_q")
+    nseq = len(cq) - 1
+    ck, pk = _host_i32(cu_seqlens_k, nseq + 1, "cu_seqlens_k")
+    qo, pqo = _host_i32(q_pos_offset, nseq, "q_pos_offset")
+    ko, pko = _host_i32(k_pos_offset, nseq, "k_pos_offset")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, t)
+    if not lse.is_cuda or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous CUDA tensor")
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("do", do)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype")
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    if v.shape != k.shape or k.shape[2] != d or tuple(do.shape) != (tq, hq, d):
+        raise ValueError("k, v must be [Tk, Hkv, D] and do [Tq, Hq, D]")
+    if o.dtype != torch.float32 or tuple(o.shape) != (tq, hq, d):
+        raise ValueError("o must be float32 [Tq, Hq, D]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (hq, tq):
+        raise ValueError("lse must be float32 [Hq, Tq]")
+    if int(cq[-1]) != tq or int(ck[-1]) != tk:
+        raise ValueError("cu_seqlens must end at the row counts of q and k")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.zeros((tq, hq, d), **f32) if dq is None else dq
+    dk = torch.zeros((tk, hkv, d), **f32) if dk is None else dk
+    dv = torch.zeros((tk, hkv, d), **f32) if dv is None else dv
+    for name, t, shp in (("dq", dq, (tq, hq, d)), ("dk", dk, (tk, hkv, d)), ("dv", dv, (tk, hkv, d))):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shp:
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shp}")
+    need = lib.cpattn_bwd_workspace_size(nseq, pq, pk, hq, hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib.cpattn_bwd_chunk(c_void_p(q.data_ptr()), c_void_p(k.data_ptr()),
+                                c_void_p(v.data_ptr()), c_void_p(o.data_ptr()),
+                                c_void_p(do.data_ptr()), c_void_p(lse.data_ptr()), pq, pk, pqo, pko,
+                                nseq, hq, hkv, d, dt, int(causal), c_void_p(dq.data_ptr()),
+                                c_void_p(dk.data_ptr()), c_void_p(dv.data_ptr()),
+                                c_void_p(workspace.data_ptr()), workspace.numel(),
+                                _stream_handle(stream)))
+    return dq, dk, dv
 
 
 def cpattn_merge(o_a, lse_a, o_b, lse_b, stream=None) -> None:

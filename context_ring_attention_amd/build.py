@@ -16,9 +16,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
 
-SOURCES = ["api.cpp", "plan.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "merge.hip"]
-# Per-source extra flags (the bf16 kernel never produces NaN; see its header comment).
-EXTRA = {"attn_fwd_bf16.hip": ["-fno-honor-nans"]}
+SOURCES = ["api.cpp", "plan.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip",
+           "merge.hip"]
+# Per-source extra flags (the bf16 kernels never produce NaN; see their header comments).
+EXTRA = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_bwd_bf16.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are disabled for all device code.

@@ -46,6 +46,25 @@ void build_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_of
                    const Geometry& g, cpattn_plan_entry* out, int64_t n_tiles,
                    cpattn_plan_info* info);
 
+// Backward, key-stationary kernel (dK, dV): a work-group owns kBwdKeysPerTile keys of one
+// kv head (kBwdWaves waves x 32 keys) and streams the query tokens that see them, in blocks
+// of kBwdQueryBlock, for every query head of the kv head's group.
+constexpr int kBwdWaves = 4;
+constexpr int kBwdKeysPerTile = 32 * kBwdWaves;
+constexpr int kBwdQueryBlock = 64;
+
+// Number of (sequence, key block) tiles of the key-stationary plan.
+int64_t count_key_tiles(const int32_t* cu_k, int32_t nseq);
+
+// Key-stationary plan entries (n_tiles, sorted longest first).  Fields are read as:
+//   row0 = first key row of the tile, nrows = its keys, k_start = first query row of the
+//   sequence, k_len = its queries, delta: query t (within the sequence) sees tile key r iff
+//   t >= delta + r (clamped to [-kBwdKeysPerTile, k_len]), cost = query blocks to visit
+//   (from max(delta, 0) to the sequence's last query), seq, tblock = key block index.
+void build_key_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_off,
+                       const int32_t* k_off, int32_t nseq, int32_t causal,
+                       cpattn_plan_entry* out, int64_t n_tiles);
+
 // Device pointers of the chunks of one launch (passed by value as a kernel argument).
 template <class T>
 struct ChunkPtrs {
@@ -66,6 +85,18 @@ hipError_t launch_attn_fwd_f32(const float* q, const ChunkPtrs<float>& kv, int n
                                const cpattn_plan_entry* plan, int n_tiles, int hq, int hkv, int d,
                                int tq_total, bool accumulate, float* o, float* lse,
                                hipStream_t stream);
+// Backward launchers: delta = rowsum(dO * O) into delta [hq, tq]; dQ over the query plan;
+// dK, dV over the key plan.
+hipError_t launch_bwd_delta(const void* do_, const float* o, int tq, int hq, int d, float* delta,
+                            hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* do_,
+                         const float* lse, const float* delta, const cpattn_plan_entry* plan,
+                         int n_tiles, int head_groups, int heads_per_tile, int hq, int hkv, int d,
+                         int tq, float* dq, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* do_,
+                           const float* lse, const float* delta, const cpattn_plan_entry* plan,
+                           int n_tiles, int hq, int hkv, int d, int tq, float* dk, float* dv,
+                           hipStream_t stream);
 hipError_t launch_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,
                         int64_t t, int hq, int d, hipStream_t stream);
 

@@ -21,8 +21,8 @@ from __future__ import annotations
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
-from ._binding import (cpattn_fwd_chunk, cpattn_fwd_chunk_accum, cpattn_fwd_chunks, cpattn_merge,
-                       cpattn_workspace_size_chunks)
+from ._binding import (cpattn_bwd_chunk, cpattn_fwd_chunk, cpattn_fwd_chunk_accum,
+                       cpattn_fwd_chunks, cpattn_merge, cpattn_workspace_size_chunks)
 
 MODES = ("stream", "accum", "merge")
 
@@ -86,3 +86,26 @@ def cpattn_share(q, ks: Sequence, vs: Sequence, cu_seqlens_q, cu_seqlens_ks: Seq
         cpattn_merge(buffers.o_acc, buffers.lse_acc, buffers.o_part, buffers.lse_part,
                      stream=stream)
     return buffers.o_acc, buffers.lse_acc
+
+
+def cpattn_share_bwd(q, ks: Sequence, vs: Sequence, o, lse, do, cu_seqlens_q,
+                     cu_seqlens_ks: Sequence, q_pos_offset=None,
+                     k_pos_offsets: Optional[Sequence] = None, causal: bool = True, stream=None):
+    """Backward of a rank's share: given the share's forward (o, lse) and the gradient do,
+    returns dq [Tq, Hq, D] (summed over the chunks) and per-chunk lists dks, dvs (fp32).
+
+    The ring's backward step order: chunk c's call adds its dq contribution and yields the
+    gradients of chunk c's keys and values (which a ring would send back to their owner).
+    """
+    import torch
+    if len(ks) == 0:
+        raise ValueError("a share needs at least one KV chunk")
+    k_pos_offsets = k_pos_offsets if k_pos_offsets is not None else [None] * len(ks)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    dks, dvs = [], []
+    for c in range(len(ks)):
+        _, dk, dv = cpattn_bwd_chunk(q, ks[c], vs[c], o, lse, do, cu_seqlens_q, cu_seqlens_ks[c],
+                                     q_pos_offset, k_pos_offsets[c], causal, dq=dq, stream=stream)
+        dks.append(dk)
+        dvs.append(dv)
+    return dq, dks, dvs

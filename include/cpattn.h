@@ -155,6 +155,46 @@ cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void
                                 hipStream_t stream);
 
 /*
+ * Backward of one KV chunk: the gradients of the attention the forward computes,
+ * i.e. of O = softmax(Q K^T / sqrt(d) + mask) V over all keys of the share, for
+ * an upstream gradient dO ("Megatron 6D parallelism guide", section 6: the
+ * ring loop is the forward of a training step; its backward is the gradient of
+ * the same function).  With P the share's probabilities (from the forward's
+ * final LSE), dP = dO V^T and dS = P * (dP - delta), delta = rowsum(dO * O),
+ * this call ADDS the chunk's contributions:
+ *     dq [Tq, hq, d]  += dS K / sqrt(d)     (sum over the chunks: call once per chunk)
+ *     dk [Tk, hkv, d] += dS^T Q / sqrt(d)   (summed over the query heads of each kv head)
+ *     dv [Tk, hkv, d] += P^T dO
+ * The caller zero-fills dq, dk, dv before the first call.
+ *
+ *   q, do_    device [Tq, hq, d] bf16           (read; do_ is the gradient of o)
+ *   k, v      device [Tk, hkv, d] bf16          (read)
+ *   o         device [Tq, hq, d] fp32           (read; the share's final forward output)
+ *   lse       device [hq, Tq] fp32              (read; the share's final forward LSE)
+ *   dq        device [Tq, hq, d] fp32; dk, dv device [Tk, hkv, d] fp32   (read and written)
+ *   metadata  as cpattn_fwd_chunk (host); dtype must be CPATTN_BF16; d in {64, 128}
+ *   workspace device, >= cpattn_bwd_workspace_size(...) bytes, 256-byte aligned; it holds
+ *             the plans and delta until the kernels have run
+ * Rows whose LSE is -inf (no visible key in the share) contribute nothing.  No output may
+ * overlap an input or another output.  Returns CPATTN_OK, or an error code with nothing
+ * enqueued (CPATTN_ERR_UNSUPPORTED for fp32 inputs).
+ */
+cpattn_status cpattn_bwd_chunk(const void* q, const void* k, const void* v, const float* o,
+                               const void* do_, const float* lse, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, const int32_t* q_pos_offset,
+                               const int32_t* k_pos_offset, int32_t nseq, int32_t hq,
+                               int32_t hkv, int32_t d, cpattn_dtype dtype, int32_t causal,
+                               float* dq, float* dk, float* dv, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace one cpattn_bwd_chunk call needs (plans of both kernels
+ * and delta [hq, Tq] fp32).  Returns 0 for invalid arguments.
+ */
+size_t cpattn_bwd_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int32_t hq, int32_t hkv, int32_t d);
+
+/*
  * The online-softmax merge of the pages' ring loop ("Megatron 6D parallelism
  * guide", section 6: m_new = max(m, m_step), alpha = exp(m - m_new),
  * beta = exp(m_step - m_new), l = alpha*l + beta*l_step, O = alpha*O + beta*O_step),

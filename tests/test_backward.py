@@ -1,0 +1,171 @@
+"""GPU parity of the backward (cpattn_bwd_chunk) against the fp64 oracle's gradients.
+
+The forward runs on the GPU (one launch over all chunks, giving the share's O and
+LSE), then the backward once per chunk: dq accumulates over the chunks, each call
+yields that chunk's dk and dv.  The oracle differentiates the unsplit attention of
+the share; dq is compared whole, dk / dv chunk by chunk against the oracle's rows
+of that chunk's keys.
+
+Tolerance (bf16 inputs, fp32 accumulation; not stated by the benchmark spec, derived here):
+P and dS are rounded to bf16 before their products (each at most 2^-8 = 3.9e-3
+relative, about 2^-9 on average, errors of both signs, so the relative L2 error of a
+sum of many such terms sits near 2^-9), and the forward's fp32 O enters
+delta = rowsum(dO * O) with the forward's own error.  The bar is the forward's
+relative L2 bound, 5e-3 per gradient, plus a max-abs error of 1e-2 of the gradient's
+largest magnitude (measured on the GPU: rel-L2 1.4-1.7e-3, max-abs 1.5-3.1e-3).
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import attention_bwd_ref, share_bwd_ref
+from parity_util import dev, host
+
+pytestmark = pytest.mark.gpu
+
+BWD_REL_L2, BWD_MAX_REL = 5e-3, 1e-2
+
+
+def check_grad(got, ref, what):
+    got = np.asarray(got, np.float64)
+    assert got.shape == ref.shape, what
+    assert np.all(np.isfinite(got)), f"non-finite gradient {what}"
+    nrm = float(np.linalg.norm(ref))
+    err = float(np.linalg.norm(got - ref))
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    worst = float(np.abs(got - ref).max()) if ref.size else 0.0
+    if nrm == 0.0:
+        assert worst <= 1e-6, f"{what}: expected zero gradient, max {worst:.3e}"
+        return 0.0
+    print(f"{what}: rel-L2 {err / nrm:.2e}, max-abs / max {worst / scale:.2e}")
+    assert err / nrm <= BWD_REL_L2, f"{what}: rel-L2 {err / nrm:.3e} > {BWD_REL_L2}"
+    assert worst <= BWD_MAX_REL * scale, f"{what}: max-abs {worst:.3e} > {BWD_MAX_REL} x {scale:.3e}"
+    return err / nrm
+
+
+def _split(rng, cu_k, ko, nchunks):
+    nseq = len(cu_k) - 1
+    cuts = [sorted(rng.integers(0, cu_k[i + 1] - cu_k[i] + 1, size=nchunks - 1).tolist())
+            for i in range(nseq)]
+    rows, cus, offs = [], [], []
+    for c in range(nchunks):
+        r, lens, off = [], [], []
+        for i in range(nseq):
+            b = [0] + cuts[i] + [int(cu_k[i + 1] - cu_k[i])]
+            r.append(np.arange(cu_k[i] + b[c], cu_k[i] + b[c + 1]))
+            lens.append(b[c + 1] - b[c])
+            off.append(int(ko[i]) + b[c])
+        rows.append(np.concatenate(r).astype(np.int64) if r else np.zeros(0, np.int64))
+        cus.append(wl.cu_from_lengths(lens))
+        offs.append(np.array(off, np.int32))
+    return rows, cus, offs
+
+
+def _run(cra, q, k, v, do, cu_q, cu_k, qo, ko, causal, nchunks, rng):
+    """GPU forward over the chunks, then per-chunk backward; returns dq and full-length dk, dv."""
+    import torch
+    rows, cus, offs = _split(rng, cu_k, ko, nchunks)
+    Q, DO = dev(q, "bfloat16"), dev(do, "bfloat16")
+    ks = [dev(k[r], "bfloat16") for r in rows]
+    vs = [dev(v[r], "bfloat16") for r in rows]
+    o, lse = cra.cpattn_fwd_chunks(Q, ks, vs, cu_q, cus, qo, offs, causal)
+    dq, dks, dvs = cra.cpattn_share_bwd(Q, ks, vs, o, lse, DO, cu_q, cus, qo, offs, causal)
+    torch.cuda.synchronize()
+    dk = np.zeros(k.shape); dv = np.zeros(v.shape)
+    for c, r in enumerate(rows):
+        dk[r] = host(dks[c]); dv[r] = host(dvs[c])
+    return host(dq), dk, dv
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 1, 128), (8, 2, 64), (4, 4, 64), (6, 3, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_random_packs(gpu_lib, hq, hkv, d, causal):
+    rng = np.random.default_rng(hq * 31 + hkv * 7 + d + causal)
+    for trial in range(2):
+        q, k, v, cu_q, cu_k, qo, ko = wl.random_pack(rng, 3, 300, hq, hkv, d, dtype="bf16",
+                                                     min_len=1, k_extra=96)
+        do = wl.round_to_bf16(rng.standard_normal(q.shape, dtype=np.float32))
+        nch = int(rng.integers(1, 5))
+        dq, dk, dv = _run(gpu_lib, q, k, v, do, cu_q, cu_k, qo, ko, causal, nch, rng)
+        rq, rk, rv = attention_bwd_ref(q, k, v, do, cu_q, cu_k, qo, ko, causal)
+        what = f"{hq}/{hkv} d={d} causal={causal} trial {trial} ({nch} chunks)"
+        check_grad(dq, rq, "dq " + what)
+        check_grad(dk, rk, "dk " + what)
+        check_grad(dv, rv, "dv " + what)
+
+
+def test_backward_empty_rows_and_sequences(gpu_lib):
+    """Empty sequences, queries before every key (LSE = -inf rows), a chunk after every query:
+    those rows and keys get exactly zero gradient, the rest match the oracle."""
+    import torch
+    rng = np.random.default_rng(5)
+    lens_q, lens_k = [0, 40, 70, 1, 33], [10, 0, 90, 5, 64]
+    cu_q, cu_k = wl.cu_from_lengths(lens_q), wl.cu_from_lengths(lens_k)
+    qo = np.array([0, 0, 10, 0, 0], np.int32)
+    ko = np.array([0, 0, 30, 0, 40], np.int32)      # sequence 2: rows 0-19 see nothing
+    q = wl.round_to_bf16(rng.standard_normal((int(cu_q[-1]), 8, 128), dtype=np.float32))
+    k = wl.round_to_bf16(rng.standard_normal((int(cu_k[-1]), 2, 128), dtype=np.float32))
+    v = wl.round_to_bf16(rng.standard_normal((int(cu_k[-1]), 2, 128), dtype=np.float32))
+    do = wl.round_to_bf16(rng.standard_normal(q.shape, dtype=np.float32))
+    dq, dk, dv = _run(gpu_lib, q, k, v, do, cu_q, cu_k, qo, ko, True, 2, rng)
+    rq, rk, rv = attention_bwd_ref(q, k, v, do, cu_q, cu_k, qo, ko, True)
+    check_grad(dq, rq, "dq"); check_grad(dk, rk, "dk"); check_grad(dv, rv, "dv")
+    assert np.all(dq[cu_q[2]:cu_q[2] + 20] == 0.0)            # rows with no visible key
+    assert np.all(dk[cu_k[4]:] == 0.0) and np.all(dv[cu_k[4]:] == 0.0)  # keys after every query
+    torch.cuda.synchronize()
+
+
+def test_backward_accumulates_and_is_deterministic(gpu_lib):
+    import torch
+    rng = np.random.default_rng(9)
+    q, k, v, cu_q, cu_k, qo, ko = wl.random_pack(rng, 3, 200, 16, 4, 128, dtype="bf16", min_len=1)
+    do = wl.round_to_bf16(rng.standard_normal(q.shape, dtype=np.float32))
+    Q, K, V, DO = (dev(x, "bfloat16") for x in (q, k, v, do))
+    o, lse = gpu_lib.cpattn_fwd_chunk(Q, K, V, cu_q, cu_k, qo, ko)
+    a = gpu_lib.cpattn_bwd_chunk(Q, K, V, o, lse, DO, cu_q, cu_k, qo, ko)
+    b = gpu_lib.cpattn_bwd_chunk(Q, K, V, o, lse, DO, cu_q, cu_k, qo, ko)
+    twice = gpu_lib.cpattn_bwd_chunk(Q, K, V, o, lse, DO, cu_q, cu_k, qo, ko,
+                                     dq=a[0].clone(), dk=a[1].clone(), dv=a[2].clone())
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, twice):
+        assert torch.equal(x, y)                      # deterministic: no atomics
+        assert torch.equal(z, x + y)                  # adds into the given buffers
+
+
+def test_backward_cp4_share_full_size_one_group(gpu_lib):
+    """The benchmarked share at full size (all heads on the GPU); the oracle differentiates
+    the first GQA group (query heads 0-3, kv head 0)."""
+    import torch
+    w = wl.make("cp4_share", 0)
+    g = w.groups[0]
+    rng = np.random.default_rng(77)
+    do = wl.round_to_bf16(rng.standard_normal(g.q.shape, dtype=np.float32))
+    Q, DO = dev(g.q, "bfloat16"), dev(do, "bfloat16")
+    ks = [dev(c.k, "bfloat16") for c in g.chunks]
+    vs = [dev(c.v, "bfloat16") for c in g.chunks]
+    cus = [c.cu_k for c in g.chunks]
+    offs = [c.k_off for c in g.chunks]
+    o, lse = gpu_lib.cpattn_fwd_chunks(Q, ks, vs, g.cu_q, cus, g.q_off, offs)
+    dq, dks, dvs = gpu_lib.cpattn_share_bwd(Q, ks, vs, o, lse, DO, g.cu_q, cus, g.q_off, offs)
+    torch.cuda.synchronize()
+    sub = wl.Group(q=g.q[:, 0:4], cu_q=g.cu_q, q_off=g.q_off, chunks=[], k_full=g.k_full[:, 0:1],
+                   v_full=g.v_full[:, 0:1], cu_full=g.cu_full)
+    rq, rk, rv = share_bwd_ref(sub, do[:, 0:4])
+    check_grad(host(dq)[:, 0:4], rq, "cp4 dq")
+    # chunk c holds piece c of every sequence: map the oracle's full-sequence key rows
+    lengths = np.diff(g.cu_full)
+    for c, ch in enumerate(g.chunks):
+        rows = np.concatenate([np.arange(g.cu_full[i] + int(ch.k_off[i]),
+                                         g.cu_full[i] + int(ch.k_off[i]) + int(ch.cu_k[i + 1] - ch.cu_k[i]))
+                               for i in range(len(lengths))])
+        check_grad(host(dks[c])[:, 0:1], rk[rows], f"cp4 dk chunk {c}")
+        check_grad(host(dvs[c])[:, 0:1], rv[rows], f"cp4 dv chunk {c}")
+
+
+def test_backward_rejects_fp32(gpu_lib):
+    import torch
+    q = torch.zeros((4, 2, 64), device="cuda")
+    lse = torch.zeros((2, 4), device="cuda")
+    with pytest.raises(gpu_lib.CpattnError) as ei:
+        gpu_lib.cpattn_bwd_chunk(q, q, q, q, lse, q, [0, 4], [0, 4])
+    assert ei.value.status == 2
