@@ -204,8 +204,8 @@ def main() -> int:
 
     backward = None
     if not args.no_backward:
-        # Backward of the share: for each chunk, cpattn_bwd_chunk adds its dq contribution and
-        # yields the chunk's dk, dv, from the share's forward (o, lse) and a synthetic gradient.
+        # Backward of the share in one pass (cpattn_bwd_chunks: dq and every chunk's dk, dv) from
+        # the share's forward (o, lse) and a synthetic gradient.
         o_f, lse_f = bufs.o_acc, bufs.lse_acc
         cra.cpattn_fwd_chunks(q, ks, vs, cu_q, cu_ks, q_off, k_offs, True, out=o_f, lse=lse_f,
                               workspace=bufs.workspace, stream=stream)
@@ -215,15 +215,13 @@ def main() -> int:
         dq = torch.zeros(q.shape, **f32)
         dks = [torch.zeros(k.shape, **f32) for k in ks]
         dvs = [torch.zeros(v.shape, **f32) for v in vs]
-        bws = torch.empty(max(cra.cpattn_bwd_workspace_size(len(cu_q) - 1, cu_q, cu_ks[0], w.hq,
-                                                            w.hkv, w.d), 256),
+        bws = torch.empty(max(cra.cpattn_bwd_workspace_size_chunks(len(cu_q) - 1, cu_q, cu_ks,
+                                                                   w.hq, w.hkv, w.d), 256),
                           dtype=torch.uint8, device="cuda")
 
         def bwd_step():
-            for c in range(nch):
-                cra.cpattn_bwd_chunk(q, ks[c], vs[c], o_f, lse_f, dout, cu_q, cu_ks[c], q_off,
-                                     k_offs[c], True, dq=dq, dk=dks[c], dv=dvs[c], workspace=bws,
-                                     stream=stream)
+            cra.cpattn_bwd_chunks(q, ks, vs, o_f, lse_f, dout, cu_q, cu_ks, q_off, k_offs, True,
+                                  dq=dq, dks=dks, dvs=dvs, workspace=bws, stream=stream)
 
         for _ in range(max(1, args.warmup)):
             bwd_step()
@@ -248,7 +246,7 @@ def main() -> int:
                     "frac": round(bwd_flops / (bwd_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                     "flops_per_step": bwd_flops,
                     "counted_as": "10 D Hq per visible pair (5 products of the forward's 2 D Hq)",
-                    "launches_per_step": f"{nch} x (delta, dQ, dK/dV)"}
+                    "launches_per_step": "delta, dQ over all chunks, dK/dV over all chunks"}
 
     import hashlib
     with open(ATTN_SOURCE, "rb") as f:

@@ -11,7 +11,7 @@ method on one GPU.
 """
 from ._binding import (  # noqa: F401
     BF16, FP32, EXPORTED, LIB_PATH, MAX_CHUNKS, PLAN_DTYPE, CpattnError, cpattn_bwd_chunk,
-    cpattn_bwd_workspace_size, cpattn_fwd_chunk,
+    cpattn_bwd_chunks, cpattn_bwd_workspace_size, cpattn_bwd_workspace_size_chunks, cpattn_fwd_chunk,
     cpattn_fwd_chunk_accum, cpattn_fwd_chunks, cpattn_merge, cpattn_plan_build,
     cpattn_plan_build_chunks, cpattn_workspace_size, cpattn_workspace_size_chunks, load,
 )

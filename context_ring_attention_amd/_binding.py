@@ -23,8 +23,9 @@ BF16, FP32 = 0, 1
 
 # Every symbol include/cpattn.h declares.
 EXPORTED = ("cpattn_workspace_size", "cpattn_workspace_size_chunks", "cpattn_fwd_chunk",
-            "cpattn_fwd_chunk_accum", "cpattn_fwd_chunks", "cpattn_bwd_chunk",
-            "cpattn_bwd_workspace_size", "cpattn_merge", "cpattn_status_string",
+            "cpattn_fwd_chunk_accum", "cpattn_fwd_chunks", "cpattn_bwd_chunk", "cpattn_bwd_chunks",
+            "cpattn_bwd_workspace_size", "cpattn_bwd_workspace_size_chunks", "cpattn_merge",
+            "cpattn_status_string",
             "cpattn_last_error", "cpattn_plan_build", "cpattn_plan_build_chunks")
 MAX_CHUNKS = 16  # CPATTN_MAX_CHUNKS
 
@@ -81,8 +82,17 @@ def load(path: str = LIB_PATH):
                                      _I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
                                      c_int32, c_int, c_int32, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_void_p]
+    lib.cpattn_bwd_chunks.restype = c_int
+    lib.cpattn_bwd_chunks.argtypes = [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int32,
+                                      c_void_p, c_void_p, c_void_p, _I32P, _I32P, _I32P, _I32P,
+                                      c_int32, c_int32, c_int32, c_int32, c_int, c_int32, c_void_p,
+                                      POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_size_t,
+                                      c_void_p]
     lib.cpattn_bwd_workspace_size.restype = c_size_t
     lib.cpattn_bwd_workspace_size.argtypes = [c_int32, _I32P, _I32P, c_int32, c_int32, c_int32]
+    lib.cpattn_bwd_workspace_size_chunks.restype = c_size_t
+    lib.cpattn_bwd_workspace_size_chunks.argtypes = [c_int32, _I32P, _I32P, c_int32, c_int32,
+                                                     c_int32, c_int32]
     lib.cpattn_merge.restype = c_int
     lib.cpattn_merge.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32,
                                  c_void_p]
@@ -392,6 +402,78 @@ def cpattn_bwd_chunk(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, q_pos_offs
                                 c_void_p(workspace.data_ptr()), workspace.numel(),
                                 _stream_handle(stream)))
     return dq, dk, dv
+
+
+def cpattn_bwd_workspace_size_chunks(nseq: int, cu_seqlens_q, cu_seqlens_ks: Sequence, hq: int,
+                                     hkv: int, d: int) -> int:
+    cq, pq = _host_i32(cu_seqlens_q, nseq + 1, "cu_seqlens_q")
+    ck, _ = _chunk_meta(cu_seqlens_ks, None, nseq)
+    return int(load().cpattn_bwd_workspace_size_chunks(nseq, pq, _ptr(ck), len(cu_seqlens_ks), hq,
+                                                        hkv, d))
+
+
+def cpattn_bwd_chunks(q, ks: Sequence, vs: Sequence, o, lse, do, cu_seqlens_q,
+                      cu_seqlens_ks: Sequence, q_pos_offset=None,
+                      k_pos_offsets: Optional[Sequence] = None, causal: bool = True, dq=None,
+                      dks: Optional[Sequence] = None, dvs: Optional[Sequence] = None,
+                      workspace=None, stream=None):
+    """Backward of all chunks in one pass: ADDS to dq and to each chunk's dk, dv (fp32 CUDA
+    tensors, zero-filled when not given); returns (dq, dks, dvs)."""
+    import torch
+    lib = load()
+    nch = len(ks)
+    if nch != len(vs) or nch != len(cu_seqlens_ks):
+        raise ValueError("ks, vs and cu_seqlens_ks must have one entry per chunk")
+    cq, pq = _host_i32(cu_seqlens_q, None, "cu_seqlens_q")
+    nseq = len(cq) - 1
+    qo, pqo = _host_i32(q_pos_offset, nseq, "q_pos_offset")
+    ck, ko = _chunk_meta(cu_seqlens_ks, k_pos_offsets, nseq)
+    for name, t in (("q", q), ("o", o), ("do", do)):
+        _check_tensor(name, t)
+    dt = _dtype_code(q)
+    tq, hq, d = q.shape
+    if do.dtype != q.dtype or tuple(do.shape) != (tq, hq, d):
+        raise ValueError("do must match q")
+    if o.dtype != torch.float32 or tuple(o.shape) != (tq, hq, d):
+        raise ValueError("o must be float32 [Tq, Hq, D]")
+    if (not lse.is_cuda or not lse.is_contiguous() or lse.dtype != torch.float32
+            or tuple(lse.shape) != (hq, tq)):
+        raise ValueError("lse must be a contiguous float32 CUDA tensor [Hq, Tq]")
+    if int(cq[-1]) != tq:
+        raise ValueError("cu_seqlens_q must end at the row count of q")
+    hkv = None
+    for c in range(nch):
+        _check_tensor(f"ks[{c}]", ks[c]); _check_tensor(f"vs[{c}]", vs[c])
+        if ks[c].dtype != q.dtype or vs[c].dtype != q.dtype or vs[c].shape != ks[c].shape:
+            raise ValueError("every chunk's k, v must be [Tk, Hkv, D] in q's dtype")
+        if hkv is not None and ks[c].shape[1] != hkv:
+            raise ValueError("every chunk must have the same kv head count")
+        hkv = ks[c].shape[1]
+        if int(ck[c, -1]) != ks[c].shape[0]:
+            raise ValueError(f"cu_seqlens_ks[{c}] must end at chunk {c}'s row count")
+    if hkv is None:
+        raise ValueError("need at least one chunk")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.zeros((tq, hq, d), **f32) if dq is None else dq
+    dks = [torch.zeros(t.shape, **f32) for t in ks] if dks is None else list(dks)
+    dvs = [torch.zeros(t.shape, **f32) for t in vs] if dvs is None else list(dvs)
+    if dq.dtype != torch.float32 or not dq.is_contiguous() or tuple(dq.shape) != (tq, hq, d):
+        raise ValueError("dq must be a contiguous float32 tensor like q")
+    for c in range(nch):
+        for name, t in (("dks", dks[c]), ("dvs", dvs[c])):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != ks[c].shape:
+                raise ValueError(f"{name}[{c}] must be a contiguous float32 tensor like ks[{c}]")
+    need = lib.cpattn_bwd_workspace_size_chunks(nseq, pq, _ptr(ck), nch, hq, hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    arr = lambda ts: (c_void_p * max(nch, 1))(*[t.data_ptr() for t in ts])
+    _check(lib.cpattn_bwd_chunks(c_void_p(q.data_ptr()), arr(ks), arr(vs), nch,
+                                 c_void_p(o.data_ptr()), c_void_p(do.data_ptr()),
+                                 c_void_p(lse.data_ptr()), pq, _ptr(ck), pqo, _ptr(ko), nseq, hq,
+                                 hkv, d, dt, int(causal), c_void_p(dq.data_ptr()), arr(dks),
+                                 arr(dvs), c_void_p(workspace.data_ptr()), workspace.numel(),
+                                 _stream_handle(stream)))
+    return dq, dks, dvs
 
 
 def cpattn_merge(o_a, lse_a, o_b, lse_b, stream=None) -> None:

@@ -312,15 +312,127 @@ BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq) {
 }
 }  // namespace
 
+size_t cpattn_bwd_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_q,
+                                        const int32_t* cu_seqlens_k, int32_t nchunks, int32_t hq,
+                                        int32_t hkv, int32_t d) {
+  (void)d;
+  if (nseq < 0 || hq < 1 || hkv < 1 || nchunks < 1 || nchunks > CPATTN_MAX_CHUNKS) return 0;
+  if (nseq > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return 0;
+  for (int32_t i = 0; i < nseq; ++i)
+    if (cu_seqlens_q[i + 1] < cu_seqlens_q[i]) return 0;
+  for (int32_t c = 0; c < nchunks; ++c)
+    for (int32_t i = 0; i < nseq; ++i)
+      if (cu_seqlens_k[int64_t(c) * (nseq + 1) + i + 1] < cu_seqlens_k[int64_t(c) * (nseq + 1) + i])
+        return 0;
+  const int64_t tq = nseq > 0 ? cu_seqlens_q[nseq] : 0;
+  return bwd_layout(count_tiles(cu_seqlens_q, nseq, kMinTileTokens) * nchunks,
+                    count_key_tiles(cu_seqlens_k, nchunks, nseq), tq, hq).total;
+}
+
 size_t cpattn_bwd_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_k, int32_t hq, int32_t hkv, int32_t d) {
-  (void)d;
-  if (nseq < 0 || hq < 1 || hkv < 1 || (nseq > 0 && (!cu_seqlens_q || !cu_seqlens_k))) return 0;
-  for (int32_t i = 0; i < nseq; ++i)
-    if (cu_seqlens_q[i + 1] < cu_seqlens_q[i] || cu_seqlens_k[i + 1] < cu_seqlens_k[i]) return 0;
-  const int64_t tq = nseq > 0 ? cu_seqlens_q[nseq] : 0;
-  return bwd_layout(count_tiles(cu_seqlens_q, nseq, kMinTileTokens),
-                    count_key_tiles(cu_seqlens_k, nseq), tq, hq).total;
+  return cpattn_bwd_workspace_size_chunks(nseq, cu_seqlens_q, cu_seqlens_k, 1, hq, hkv, d);
+}
+
+cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void* const* vs,
+                                int32_t nchunks, const float* o, const void* do_,
+                                const float* lse, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const int32_t* q_pos_offset,
+                                const int32_t* k_pos_offset, int32_t nseq, int32_t hq,
+                                int32_t hkv, int32_t d, cpattn_dtype dtype, int32_t causal,
+                                float* dq, float* const* dks, float* const* dvs, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  if (dtype != CPATTN_BF16 && dtype != CPATTN_FP32)
+    return set_error(CPATTN_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  if (nchunks >= 1 && nchunks <= CPATTN_MAX_CHUNKS && (!ks || !vs || !dks || !dvs))
+    return set_error(CPATTN_ERR_INVALID_ARG, "chunk pointer arrays must be non-null");
+  cpattn_status st = validate_metadata(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset,
+                                       nchunks, nseq, hq, hkv, d);
+  if (st != CPATTN_OK) return st;
+  if (dtype != CPATTN_BF16)
+    return set_error(CPATTN_ERR_UNSUPPORTED, "the backward takes bf16 inputs only");
+  const int64_t tq = cu_seqlens_q[nseq];
+  if (tq == 0) return CPATTN_OK;  // no query, nothing to add
+  if (!q || !o || !do_ || !lse || !dq)
+    return set_error(CPATTN_ERR_INVALID_ARG, "every tensor must be non-null");
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(do_, 16) || !aligned(lse, 4) || !aligned(dq, 16))
+    return set_error(CPATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned and lse 4-byte aligned");
+  const size_t qb = size_t(tq) * hq * d * 2;
+  const size_t of = size_t(tq) * hq * d * 4, lb = size_t(tq) * hq * 4;
+  // Every output region against every input region and every other output region.
+  std::vector<const void*> in_p = {q, o, do_, lse};
+  std::vector<size_t> in_b = {qb, of, qb, lb};
+  std::vector<const void*> out_p = {dq};
+  std::vector<size_t> out_b = {of};
+  for (int32_t c = 0; c < nchunks; ++c) {
+    const int64_t tk = cu_seqlens_k[int64_t(c) * (nseq + 1) + nseq];
+    if (tk == 0) continue;
+    if (!ks[c] || !vs[c] || !dks[c] || !dvs[c])
+      return set_error(CPATTN_ERR_INVALID_ARG, "chunk %d: k, v, dk and dv must be non-null", c);
+    if (!aligned(ks[c], 16) || !aligned(vs[c], 16) || !aligned(dks[c], 16) || !aligned(dvs[c], 16))
+      return set_error(CPATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned and lse 4-byte aligned");
+    const size_t kb = size_t(tk) * hkv * d * 2, kf = size_t(tk) * hkv * d * 4;
+    in_p.push_back(ks[c]); in_b.push_back(kb);
+    in_p.push_back(vs[c]); in_b.push_back(kb);
+    out_p.push_back(dks[c]); out_b.push_back(kf);
+    out_p.push_back(dvs[c]); out_b.push_back(kf);
+  }
+  for (size_t a = 0; a < out_p.size(); ++a) {
+    for (size_t b = 0; b < in_p.size(); ++b)
+      if (overlaps(out_p[a], out_b[a], in_p[b], in_b[b]))
+        return set_error(CPATTN_ERR_INVALID_ARG, "gradients must not overlap any input");
+    for (size_t b = a + 1; b < out_p.size(); ++b)
+      if (overlaps(out_p[a], out_b[a], out_p[b], out_b[b]))
+        return set_error(CPATTN_ERR_INVALID_ARG, "gradients must not overlap each other");
+  }
+  const Geometry g = geometry_for(CPATTN_BF16, hq, hkv);
+  const int64_t n_qt = count_tiles(cu_seqlens_q, nseq, g.tokens_per_tile);
+  const BwdLayout lay = bwd_layout(n_qt * nchunks, count_key_tiles(cu_seqlens_k, nchunks, nseq),
+                                   tq, hq);
+  if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256))
+    return set_error(CPATTN_ERR_WORKSPACE, "workspace of %zu bytes (need %zu, 256-byte aligned)",
+                     workspace_bytes, lay.total);
+  const int head_groups = hq / g.heads_per_tile;
+  if (n_qt * head_groups > int64_t(INT32_MAX) || lay.n_k * hkv > int64_t(INT32_MAX) ||
+      n_qt * nchunks > int64_t(INT32_MAX))
+    return set_error(CPATTN_ERR_UNSUPPORTED, "too many tiles for one launch");
+  char* ws = static_cast<char*>(workspace);
+  for (size_t a = 0; a < out_p.size(); ++a)
+    if (overlaps(out_p[a], out_b[a], ws, lay.total))
+      return set_error(CPATTN_ERR_INVALID_ARG, "the workspace must not overlap the gradients");
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(CPATTN_ERR_HIP, "hipGetDevice failed");
+  st = g_rings[dev].upload(workspace, lay.plan_bytes, stream, [&](char* dst) {
+    build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal, g,
+                  reinterpret_cast<cpattn_plan_entry*>(dst), n_qt, nullptr);
+    build_key_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq,
+                      causal, reinterpret_cast<KeyTile*>(dst + lay.key_plan_at), lay.n_k);
+  });
+  if (st != CPATTN_OK) return st;
+  const auto* qplan = reinterpret_cast<const cpattn_plan_entry*>(ws);
+  const auto* kplan = reinterpret_cast<const KeyTile*>(ws + lay.key_plan_at);
+  float* delta = reinterpret_cast<float*>(ws + lay.delta_at);
+  ChunkPtrs<__bf16> kv{};
+  ChunkPtrs<float> dkv{};
+  for (int32_t c = 0; c < nchunks; ++c) {
+    kv.k[c] = static_cast<const __bf16*>(ks[c]);
+    kv.v[c] = static_cast<const __bf16*>(vs[c]);
+    dkv.k[c] = dks[c];
+    dkv.v[c] = dvs[c];
+  }
+  hipError_t err = launch_bwd_delta(do_, o, int(tq), hq, d, delta, stream);
+  if (err == hipSuccess)
+    err = launch_bwd_dq(q, kv, nchunks, do_, lse, delta, qplan, int(n_qt), head_groups,
+                        g.heads_per_tile, hq, hkv, d, int(tq), dq, stream);
+  if (err == hipSuccess)
+    err = launch_bwd_dkdv(q, kv, do_, lse, delta, kplan, int(lay.n_k), hq, hkv, d, int(tq), dkv,
+                          stream);
+  if (err != hipSuccess)
+    return set_error(CPATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
+  return CPATTN_OK;
 }
 
 cpattn_status cpattn_bwd_chunk(const void* q, const void* k, const void* v, const float* o,
@@ -330,72 +442,9 @@ cpattn_status cpattn_bwd_chunk(const void* q, const void* k, const void* v, cons
                                int32_t hkv, int32_t d, cpattn_dtype dtype, int32_t causal,
                                float* dq, float* dk, float* dv, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-  clear_error();
-  if (dtype != CPATTN_BF16 && dtype != CPATTN_FP32)
-    return set_error(CPATTN_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
-  cpattn_status st = validate_metadata(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, 1,
-                                       nseq, hq, hkv, d);
-  if (st != CPATTN_OK) return st;
-  if (dtype != CPATTN_BF16)
-    return set_error(CPATTN_ERR_UNSUPPORTED, "the backward takes bf16 inputs only");
-  const int64_t tq = cu_seqlens_q[nseq], tk = cu_seqlens_k[nseq];
-  if (tq == 0 || tk == 0) return CPATTN_OK;  // no pair, nothing to add
-  if (!q || !k || !v || !o || !do_ || !lse || !dq || !dk || !dv)
-    return set_error(CPATTN_ERR_INVALID_ARG, "every tensor must be non-null");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(do_, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
-    return set_error(CPATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned and lse 4-byte aligned");
-  const size_t qb = size_t(tq) * hq * d * 2, kb = size_t(tk) * hkv * d * 2;
-  const size_t of = size_t(tq) * hq * d * 4, lb = size_t(tq) * hq * 4, kf = size_t(tk) * hkv * d * 4;
-  const void* ins[6] = {q, k, v, o, do_, lse};
-  const size_t in_bytes[6] = {qb, kb, kb, of, qb, lb};
-  float* outs[3] = {dq, dk, dv};
-  const size_t out_bytes[3] = {of, kf, kf};
-  for (int a = 0; a < 3; ++a) {
-    for (int b = 0; b < 6; ++b)
-      if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b]))
-        return set_error(CPATTN_ERR_INVALID_ARG, "dq, dk and dv must not overlap any input");
-    for (int b = a + 1; b < 3; ++b)
-      if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b]))
-        return set_error(CPATTN_ERR_INVALID_ARG, "dq, dk and dv must not overlap each other");
-  }
-  const Geometry g = geometry_for(CPATTN_BF16, hq, hkv);
-  const BwdLayout lay = bwd_layout(count_tiles(cu_seqlens_q, nseq, g.tokens_per_tile),
-                                   count_key_tiles(cu_seqlens_k, nseq), tq, hq);
-  if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256))
-    return set_error(CPATTN_ERR_WORKSPACE, "workspace of %zu bytes (need %zu, 256-byte aligned)",
-                     workspace_bytes, lay.total);
-  const int head_groups = hq / g.heads_per_tile;
-  if (lay.n_q * head_groups > int64_t(INT32_MAX) || lay.n_k * hkv > int64_t(INT32_MAX))
-    return set_error(CPATTN_ERR_UNSUPPORTED, "too many tiles for one launch");
-  char* ws = static_cast<char*>(workspace);
-  for (int a = 0; a < 3; ++a)
-    if (overlaps(outs[a], out_bytes[a], ws, lay.total))
-      return set_error(CPATTN_ERR_INVALID_ARG, "the workspace must not overlap dq, dk or dv");
-
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return set_error(CPATTN_ERR_HIP, "hipGetDevice failed");
-  st = g_rings[dev].upload(workspace, lay.plan_bytes, stream, [&](char* dst) {
-    build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, 1, nseq, causal, g,
-                  reinterpret_cast<cpattn_plan_entry*>(dst), lay.n_q, nullptr);
-    build_key_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq, causal,
-                      reinterpret_cast<cpattn_plan_entry*>(dst + lay.key_plan_at), lay.n_k);
-  });
-  if (st != CPATTN_OK) return st;
-  const auto* qplan = reinterpret_cast<const cpattn_plan_entry*>(ws);
-  const auto* kplan = reinterpret_cast<const cpattn_plan_entry*>(ws + lay.key_plan_at);
-  float* delta = reinterpret_cast<float*>(ws + lay.delta_at);
-  hipError_t err = launch_bwd_delta(do_, o, int(tq), hq, d, delta, stream);
-  if (err == hipSuccess)
-    err = launch_bwd_dq(q, k, v, do_, lse, delta, qplan, int(lay.n_q), head_groups,
-                        g.heads_per_tile, hq, hkv, d, int(tq), dq, stream);
-  if (err == hipSuccess)
-    err = launch_bwd_dkdv(q, k, v, do_, lse, delta, kplan, int(lay.n_k), hq, hkv, d, int(tq), dk,
-                          dv, stream);
-  if (err != hipSuccess)
-    return set_error(CPATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
-  return CPATTN_OK;
+  return cpattn_bwd_chunks(q, &k, &v, 1, o, do_, lse, cu_seqlens_q, cu_seqlens_k, q_pos_offset,
+                           k_pos_offset, nseq, hq, hkv, d, dtype, causal, dq, &dk, &dv, workspace,
+                           workspace_bytes, stream);
 }
 
 cpattn_status cpattn_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,

@@ -7,12 +7,15 @@
 //   dQ += dS K / sqrt(D),   dK += dS^T Q / sqrt(D),   dV += P^T dO.
 // Three kernels, no atomics (results are deterministic):
 //   bwd_delta   delta [hq, Tq] = rowsum(dO * O), HBM-bound;
-//   bwd_dq      query-stationary, the forward's tiling: per 64-key block
-//               S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T;
-//   bwd_dkdv    key-stationary: a work-group owns 128 keys of one kv head (32 per
-//               wave, K and V fragments held in registers) and streams the query
-//               tokens that see them, 64 at a time, for every query head of the
-//               group: S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.
+//   bwd_dq      query-stationary, the forward's tiling and its walk over the KV
+//               chunks: per 64-key block S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, then
+//               dQ^T += K^T dS^T; dQ is written once per launch;
+//   bwd_dkdv    key-stationary: a work-group owns 128 keys of one kv head in one
+//               chunk (32 per wave, K and V fragments held in registers) and streams
+//               the query tokens that see them, 64 at a time, for every query head
+//               of the group: S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P,
+//               dK^T += Q^T dS.  One launch covers the key tiles of every chunk,
+//               longest first.
 // Matrix-core mapping: every product is a v_mfma_f32_32x32x16_bf16 whose result
 // keeps one column index per lane (lane % 32) and 16 row indices per lane, like the
 // forward's S^T tile; the probability-like results (P, dS) are rounded to bf16 and
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const __bf16* __res
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ q, const ChunkPtrs<__bf16> kv, int nchunks,
     const __bf16* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, const cpattn_plan_entry* __restrict__ plan,
     int head_groups, int heads_per_tile, int hq, int hkv, int tq, float scale, float scale_log2,
@@ -206,17 +209,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int b = blockIdx.x;
   const int e = b / head_groups;
   const int hg = b - e * head_groups;
-  const cpattn_plan_entry pe = plan[e];
+  const cpattn_plan_entry* tile = plan + int64_t(e) * nchunks;  // one entry per chunk
   const int head = hg * heads_per_tile + (wave % heads_per_tile);
   const int tok0 = (wave / heads_per_tile) * kBf16RowsPerWave;
   const int kvh = (hg * heads_per_tile) / (hq / hkv);
-  const int rows_w = min(max(pe.nrows - tok0, 0), kBf16RowsPerWave);
+  const int rows_w = min(max(tile[0].nrows - tok0, 0), kBf16RowsPerWave);
 
   // B operands (token n's row of Q and of dO), the row's effective LSE (log2 units; +inf
   // for rows outside the tile or with no visible key: their P is 0) and delta.
   bf16x8 qf[KS], dof[KS];
   const bool ok = n < rows_w;
-  const int64_t row = pe.row0 + tok0 + n;
+  const int64_t row = tile[0].row0 + tok0 + n;
   {
     const __bf16* qp = q + (row * hq + head) * D + 8 * g;
     const __bf16* dp = dout + (row * hq + head) * D + 8 * g;
@@ -230,52 +233,65 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const float lse_eff = lse_row == -INFINITY ? INFINITY : lse_row * 1.4426950408889634f;
   const float delta_row = ok ? delta[int64_t(head) * tq + row] : 0.f;
 
-  int nblk_w = 0, nfull_w = 0;
-  if (rows_w > 0) {
-    const int kend = max(0, min(pe.k_len, pe.delta + tok0 + rows_w));
-    nblk_w = (kend + BN - 1) / BN;
-    nfull_w = min(min(pe.k_len / BN, max(0, pe.delta + tok0 + 1) / BN), nblk_w);
-  }
-  const int nblk = pe.cost;
-
   f32x16 acc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
 
-  auto issue = [&](int j, int stage) {
+  // Block j of chunk c into LDS stage `stage`: K (read by rows and transposed), then V.
+  auto issue = [&](int c, int j, int stage) {
     char* s = smem + stage * kStage;
-    const int64_t first = int64_t(pe.k_start) + int64_t(j) * BN;
-    const int64_t left = int64_t(pe.k_len) - int64_t(j) * BN;
-    load_tile<D, true>(k, first, kvh, hkv, left, s, wave, lane);
-    load_tile<D, false>(v, first, kvh, hkv, left, s + T::kBytes, wave, lane);
+    const int64_t first = int64_t(tile[c].k_start) + int64_t(j) * BN;
+    const int64_t left = int64_t(tile[c].k_len) - int64_t(j) * BN;
+    load_tile<D, true>(kv.k[c], first, kvh, hkv, left, s, wave, lane);
+    load_tile<D, false>(kv.v[c], first, kvh, hkv, left, s + T::kBytes, wave, lane);
+  };
+  auto next_chunk = [&](int c) {
+    ++c;
+    while (c < nchunks && tile[c].cost == 0) ++c;
+    return c;
   };
 
-  if (nblk > 0) issue(0, 0);
-  for (int j = 0; j < nblk; ++j) {
-    const int stage = j & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 1 < nblk) issue(j + 1, stage ^ 1);
-    if (j < nblk_w) {
-      const char* kt = smem + stage * kStage;
-      const char* vt = kt + T::kBytes;
-      f32x16 s0, s1, p0, p1;
-      rows_product<D, true>(kt, qf, n, g, s0, s1);        // S^T = K Q^T
-      rows_product<D, false>(vt, dof, n, g, p0, p1);      // dP^T = V dO^T
-      const int lim = (j >= nfull_w) ? min(pe.k_len - 1, pe.delta + tok0 + n) - j * BN - 4 * g
-                                     : BN;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kin = 8 * (r >> 2) + (r & 3);
-        const float e0 = kin > lim ? 0.f : __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -lse_eff));
-        const float e1 = 32 + kin > lim ? 0.f : __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -lse_eff));
-        s0[r] = e0 * (p0[r] - delta_row);                  // dS^T
-        s1[r] = e1 * (p1[r] - delta_row);
-      }
-      bf16x8 dsb[4];
-      pack_b(s0, s1, dsb);
-      transposed_product<D>(kt, dsb, n, g, acc);           // dQ^T += K^T dS^T
+  int stage = 0;
+  int c = next_chunk(-1);
+  if (c < nchunks) issue(c, 0, 0);
+  for (; c < nchunks;) {
+    const cpattn_plan_entry pe = tile[c];
+    const int cn = next_chunk(c);
+    int nblk_w = 0, nfull_w = 0;
+    if (rows_w > 0) {
+      const int kend = max(0, min(pe.k_len, pe.delta + tok0 + rows_w));
+      nblk_w = (kend + BN - 1) / BN;
+      nfull_w = min(min(pe.k_len / BN, max(0, pe.delta + tok0 + 1) / BN), nblk_w);
     }
+    const int nblk = pe.cost;
+    for (int j = 0; j < nblk; ++j, stage ^= 1) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 1 < nblk) issue(c, j + 1, stage ^ 1);
+      else if (cn < nchunks) issue(cn, 0, stage ^ 1);
+      if (j < nblk_w) {
+        const char* kt = smem + stage * kStage;
+        const char* vt = kt + T::kBytes;
+        f32x16 s0, s1, p0, p1;
+        rows_product<D, true>(kt, qf, n, g, s0, s1);        // S^T = K Q^T
+        rows_product<D, false>(vt, dof, n, g, p0, p1);      // dP^T = V dO^T
+        const int lim = (j >= nfull_w) ? min(pe.k_len - 1, pe.delta + tok0 + n) - j * BN - 4 * g
+                                       : BN;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kin = 8 * (r >> 2) + (r & 3);
+          const float e0 = kin > lim ? 0.f : __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -lse_eff));
+          const float e1 =
+              32 + kin > lim ? 0.f : __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -lse_eff));
+          s0[r] = e0 * (p0[r] - delta_row);                  // dS^T
+          s1[r] = e1 * (p1[r] - delta_row);
+        }
+        bf16x8 dsb[4];
+        pack_b(s0, s1, dsb);
+        transposed_product<D>(kt, dsb, n, g, acc);           // dQ^T += K^T dS^T
+      }
+    }
+    c = cn;
   }
 
   if (ok) {
@@ -300,10 +316,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, const cpattn_plan_entry* __restrict__ plan, int hq, int hkv,
-    int tq, float scale, float scale_log2, float* __restrict__ dk, float* __restrict__ dv) {
+    const __bf16* __restrict__ q, const ChunkPtrs<__bf16> kv, const __bf16* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    const KeyTile* __restrict__ plan, int hq, int hkv, int tq, float scale, float scale_log2,
+    const ChunkPtrs<float> dkv) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = Tile<D>;
   constexpr int KS = D / 16;
@@ -318,7 +334,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int g = lane >> 5;
   const int e = blockIdx.x / hkv;
   const int kvh = blockIdx.x - e * hkv;
-  const cpattn_plan_entry pe = plan[e];
+  const KeyTile pe = plan[e];
+  const __bf16* k = kv.k[pe.chunk];
+  const __bf16* v = kv.v[pe.chunk];
   const int group = hq / hkv;
   const int key = 32 * wave + n;          // this lane's key within the tile
   const bool key_ok = key < pe.nrows;
@@ -348,8 +366,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   auto issue = [&](int step, int stage) {
     const int hi = step / nblk, j = step - hi * nblk;
     const int h = kvh * group + hi;
-    const int64_t first = int64_t(pe.k_start) + t_first + int64_t(j) * QB;
-    const int64_t left = int64_t(pe.k_len) - t_first - int64_t(j) * QB;
+    const int64_t first = int64_t(pe.q_start) + t_first + int64_t(j) * QB;
+    const int64_t left = int64_t(pe.q_len) - t_first - int64_t(j) * QB;
     char* s = smem + stage * kStage;
     load_tile<D, true>(q, first, h, hq, left, s, wave, lane);
     load_tile<D, true>(dout, first, h, hq, left, s + T::kBytes, wave, lane);
@@ -378,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // Query (within the sequence) of register r of tile tt: t_first + 64 j + 32 tt + 8 (r / 4)
     // + 4 g + r % 4; visible iff it is < k_len and >= delta + key.
     const int tb = t_first + j * QB + 4 * g;
-    const int lo = pe.delta + key, hi_excl = pe.k_len;
+    const int lo = pe.delta + key, hi_excl = pe.q_len;
     bf16x8 pb[4], db[4];
     {
       f32x16 ps0, ps1;
@@ -407,8 +425,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
 
   if (key_ok) {
-    float* kp = dk + (krow * hkv + kvh) * D + 4 * g;
-    float* vp = dv + (krow * hkv + kvh) * D + 4 * g;
+    float* kp = const_cast<float*>(dkv.k[pe.chunk]) + (krow * hkv + kvh) * D + 4 * g;
+    float* vp = const_cast<float*>(dkv.v[pe.chunk]) + (krow * hkv + kvh) * D + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -447,7 +465,7 @@ hipError_t launch_bwd_delta(const void* do_, const float* o, int tq, int hq, int
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* do_,
+hipError_t launch_bwd_dq(const void* q, const ChunkPtrs<__bf16>& kv, int nchunks, const void* do_,
                          const float* lse, const float* delta, const cpattn_plan_entry* plan,
                          int n_tiles, int head_groups, int heads_per_tile, int hq, int hkv, int d,
                          int tq, float* dq, hipStream_t stream) {
@@ -456,9 +474,8 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   const float scale = 1.0f / sqrtf(float(d));
   const float scale_log2 = scale * 1.4426950408889634f;
   auto launch = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const __bf16*>(q),
-                       static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-                       static_cast<const __bf16*>(do_), lse, delta, plan, head_groups,
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const __bf16*>(q), kv,
+                       nchunks, static_cast<const __bf16*>(do_), lse, delta, plan, head_groups,
                        heads_per_tile, hq, hkv, tq, scale, scale_log2, dq);
   };
   if (d == 128) launch(bwd_dq_kernel<128>);
@@ -467,19 +484,18 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* do_,
-                           const float* lse, const float* delta, const cpattn_plan_entry* plan,
-                           int n_tiles, int hq, int hkv, int d, int tq, float* dk, float* dv,
+hipError_t launch_bwd_dkdv(const void* q, const ChunkPtrs<__bf16>& kv, const void* do_,
+                           const float* lse, const float* delta, const KeyTile* plan, int n_tiles,
+                           int hq, int hkv, int d, int tq, const ChunkPtrs<float>& dkv,
                            hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   const dim3 grid(unsigned(n_tiles) * unsigned(hkv));
   const float scale = 1.0f / sqrtf(float(d));
   const float scale_log2 = scale * 1.4426950408889634f;
   auto launch = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const __bf16*>(q),
-                       static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const __bf16*>(q), kv,
                        static_cast<const __bf16*>(do_), lse, delta, plan, hq, hkv, tq, scale,
-                       scale_log2, dk, dv);
+                       scale_log2, dkv);
   };
   if (d == 128) launch(bwd_dkdv_kernel<128>);
   else if (d == 64) launch(bwd_dkdv_kernel<64>);

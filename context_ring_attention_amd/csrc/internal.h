@@ -53,17 +53,28 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdKeysPerTile = 32 * kBwdWaves;
 constexpr int kBwdQueryBlock = 64;
 
-// Number of (sequence, key block) tiles of the key-stationary plan.
-int64_t count_key_tiles(const int32_t* cu_k, int32_t nseq);
+// One tile of the key-stationary plan: kBwdKeysPerTile keys of one sequence in one chunk.
+struct KeyTile {
+  int32_t row0;     // first key row of the tile (in its chunk's K / V)
+  int32_t nrows;    // keys in the tile
+  int32_t q_start;  // first query row of the sequence
+  int32_t q_len;    // queries of the sequence
+  int32_t delta;    // query t (within the sequence) sees tile key r iff t >= delta + r,
+                    // clamped to [-kBwdKeysPerTile, q_len]
+  int32_t cost;     // query blocks to visit, from max(delta, 0) to the last query
+  int32_t chunk;    // chunk of the tile's keys
+  int32_t pad;
+};
+static_assert(sizeof(KeyTile) == 32, "plan records are 32 bytes");
 
-// Key-stationary plan entries (n_tiles, sorted longest first).  Fields are read as:
-//   row0 = first key row of the tile, nrows = its keys, k_start = first query row of the
-//   sequence, k_len = its queries, delta: query t (within the sequence) sees tile key r iff
-//   t >= delta + r (clamped to [-kBwdKeysPerTile, k_len]), cost = query blocks to visit
-//   (from max(delta, 0) to the sequence's last query), seq, tblock = key block index.
+// Number of (chunk, sequence, key block) tiles of the key-stationary plan (cu_k is
+// [nchunks][nseq + 1]).
+int64_t count_key_tiles(const int32_t* cu_k, int32_t nchunks, int32_t nseq);
+
+// Key-stationary plan over nchunks chunks, sorted by cost, longest first.
 void build_key_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_off,
-                       const int32_t* k_off, int32_t nseq, int32_t causal,
-                       cpattn_plan_entry* out, int64_t n_tiles);
+                       const int32_t* k_off, int32_t nchunks, int32_t nseq, int32_t causal,
+                       KeyTile* out, int64_t n_tiles);
 
 // Device pointers of the chunks of one launch (passed by value as a kernel argument).
 template <class T>
@@ -85,17 +96,17 @@ hipError_t launch_attn_fwd_f32(const float* q, const ChunkPtrs<float>& kv, int n
                                const cpattn_plan_entry* plan, int n_tiles, int hq, int hkv, int d,
                                int tq_total, bool accumulate, float* o, float* lse,
                                hipStream_t stream);
-// Backward launchers: delta = rowsum(dO * O) into delta [hq, tq]; dQ over the query plan;
-// dK, dV over the key plan.
+// Backward launchers: delta = rowsum(dO * O) into delta [hq, tq]; dQ over the query plan
+// (tile-major over nchunks chunks, as the forward's); dK, dV over the key plan.
 hipError_t launch_bwd_delta(const void* do_, const float* o, int tq, int hq, int d, float* delta,
                             hipStream_t stream);
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* do_,
+hipError_t launch_bwd_dq(const void* q, const ChunkPtrs<__bf16>& kv, int nchunks, const void* do_,
                          const float* lse, const float* delta, const cpattn_plan_entry* plan,
                          int n_tiles, int head_groups, int heads_per_tile, int hq, int hkv, int d,
                          int tq, float* dq, hipStream_t stream);
-hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* do_,
-                           const float* lse, const float* delta, const cpattn_plan_entry* plan,
-                           int n_tiles, int hq, int hkv, int d, int tq, float* dk, float* dv,
+hipError_t launch_bwd_dkdv(const void* q, const ChunkPtrs<__bf16>& kv, const void* do_,
+                           const float* lse, const float* delta, const KeyTile* plan, int n_tiles,
+                           int hq, int hkv, int d, int tq, const ChunkPtrs<float>& dkv,
                            hipStream_t stream);
 hipError_t launch_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,
                         int64_t t, int hq, int d, hipStream_t stream);

@@ -172,43 +172,49 @@ void build_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_of
   }
 }
 
-int64_t count_key_tiles(const int32_t* cu_k, int32_t nseq) {
+int64_t count_key_tiles(const int32_t* cu_k, int32_t nchunks, int32_t nseq) {
   int64_t n = 0;
-  for (int32_t i = 0; i < nseq; ++i) {
-    const int64_t len = int64_t(cu_k[i + 1]) - cu_k[i];
-    n += (len + kBwdKeysPerTile - 1) / kBwdKeysPerTile;
+  for (int32_t c = 0; c < nchunks; ++c) {
+    const int32_t* ck = cu_k + int64_t(c) * (nseq + 1);
+    for (int32_t i = 0; i < nseq; ++i) {
+      const int64_t len = int64_t(ck[i + 1]) - ck[i];
+      n += (len + kBwdKeysPerTile - 1) / kBwdKeysPerTile;
+    }
   }
   return n;
 }
 
 void build_key_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_off,
-                       const int32_t* k_off, int32_t nseq, int32_t causal,
-                       cpattn_plan_entry* out, int64_t n_tiles) {
+                       const int32_t* k_off, int32_t nchunks, int32_t nseq, int32_t causal,
+                       KeyTile* out, int64_t n_tiles) {
   const int kt = kBwdKeysPerTile, qb = kBwdQueryBlock;
   int64_t e = 0;
-  for (int32_t i = 0; i < nseq; ++i) {
-    const int32_t nq = cu_q[i + 1] - cu_q[i], nk = cu_k[i + 1] - cu_k[i];
-    const int64_t qo = q_off ? q_off[i] : 0, ko = k_off ? k_off[i] : 0;
-    for (int32_t tb = 0; tb * int64_t(kt) < nk; ++tb) {
-      cpattn_plan_entry p;
-      p.row0 = cu_k[i] + tb * kt;
-      p.nrows = std::min<int32_t>(kt, nk - tb * kt);
-      p.k_start = cu_q[i];
-      p.k_len = nq;
-      // key u = kt tb + r sits at ko + u; query t at qo + t sees it iff t >= ko + u - qo
-      int64_t delta = causal ? (ko + int64_t(tb) * kt - qo) : int64_t(-kt);
-      delta = std::max<int64_t>(-kt, std::min<int64_t>(delta, nq));
-      p.delta = int32_t(delta);
-      const int64_t first = std::max<int64_t>(0, delta);
-      p.cost = int32_t((nq - first + qb - 1) / qb);
-      p.seq = i;
-      p.tblock = tb;
-      out[e++] = p;
+  for (int32_t c = 0; c < nchunks; ++c) {
+    const int32_t* ck = cu_k + int64_t(c) * (nseq + 1);
+    for (int32_t i = 0; i < nseq; ++i) {
+      const int32_t nq = cu_q[i + 1] - cu_q[i], nk = ck[i + 1] - ck[i];
+      const int64_t qo = q_off ? q_off[i] : 0, ko = k_off ? k_off[int64_t(c) * nseq + i] : 0;
+      for (int32_t tb = 0; tb * int64_t(kt) < nk; ++tb) {
+        KeyTile p;
+        p.row0 = ck[i] + tb * kt;
+        p.nrows = std::min<int32_t>(kt, nk - tb * kt);
+        p.q_start = cu_q[i];
+        p.q_len = nq;
+        // key u = kt tb + r sits at ko + u; query t at qo + t sees it iff t >= ko + u - qo
+        int64_t delta = causal ? (ko + int64_t(tb) * kt - qo) : int64_t(-kt);
+        delta = std::max<int64_t>(-kt, std::min<int64_t>(delta, nq));
+        p.delta = int32_t(delta);
+        const int64_t first = std::max<int64_t>(0, delta);
+        p.cost = int32_t((nq - first + qb - 1) / qb);
+        p.chunk = c;
+        p.pad = 0;
+        out[e++] = p;
+      }
     }
   }
-  std::stable_sort(out, out + n_tiles, [](const cpattn_plan_entry& a, const cpattn_plan_entry& b) {
-    return a.cost > b.cost;
-  });
+  // Longest first; ties keep (chunk, sequence, block) order.
+  std::stable_sort(out, out + n_tiles,
+                   [](const KeyTile& a, const KeyTile& b) { return a.cost > b.cost; });
 }
 
 }  // namespace cpattn

@@ -21,8 +21,9 @@ from __future__ import annotations
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
-from ._binding import (cpattn_bwd_chunk, cpattn_fwd_chunk, cpattn_fwd_chunk_accum,
-                       cpattn_fwd_chunks, cpattn_merge, cpattn_workspace_size_chunks)
+from ._binding import (cpattn_bwd_chunk, cpattn_bwd_chunks, cpattn_fwd_chunk,
+                       cpattn_fwd_chunk_accum, cpattn_fwd_chunks, cpattn_merge,
+                       cpattn_workspace_size_chunks)
 
 MODES = ("stream", "accum", "merge")
 
@@ -90,16 +91,22 @@ def cpattn_share(q, ks: Sequence, vs: Sequence, cu_seqlens_q, cu_seqlens_ks: Seq
 
 def cpattn_share_bwd(q, ks: Sequence, vs: Sequence, o, lse, do, cu_seqlens_q,
                      cu_seqlens_ks: Sequence, q_pos_offset=None,
-                     k_pos_offsets: Optional[Sequence] = None, causal: bool = True, stream=None):
+                     k_pos_offsets: Optional[Sequence] = None, causal: bool = True, stream=None,
+                     per_chunk: bool = False):
     """Backward of a rank's share: given the share's forward (o, lse) and the gradient do,
     returns dq [Tq, Hq, D] (summed over the chunks) and per-chunk lists dks, dvs (fp32).
 
-    The ring's backward step order: chunk c's call adds its dq contribution and yields the
-    gradients of chunk c's keys and values (which a ring would send back to their owner).
+    Default: one cpattn_bwd_chunks pass over all chunks.  per_chunk=True takes the ring's
+    backward step order instead, one cpattn_bwd_chunk call per chunk, each adding its dq
+    contribution and yielding the gradients of that chunk's keys and values (which a ring
+    would send back to their owner).
     """
     import torch
     if len(ks) == 0:
         raise ValueError("a share needs at least one KV chunk")
+    if not per_chunk:
+        return cpattn_bwd_chunks(q, ks, vs, o, lse, do, cu_seqlens_q, cu_seqlens_ks, q_pos_offset,
+                                 k_pos_offsets, causal, stream=stream)
     k_pos_offsets = k_pos_offsets if k_pos_offsets is not None else [None] * len(ks)
     dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
     dks, dvs = [], []

@@ -188,11 +188,37 @@ cpattn_status cpattn_bwd_chunk(const void* q, const void* k, const void* v, cons
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Backward of every KV chunk of a share in one pass (the backward of cpattn_fwd_chunks):
+ * delta is formed once, one dQ launch walks all chunks (dq gets the whole share's
+ * gradient in one write), and one dK/dV launch covers the key tiles of every chunk.
+ * ADDS to dq, dks[c], dvs[c] exactly what nchunks cpattn_bwd_chunk calls would (up to
+ * rounding order).
+ *   ks, vs      HOST arrays of nchunks device pointers, chunk c [Tk_c, hkv, d] bf16
+ *   dks, dvs    HOST arrays of nchunks device pointers, chunk c [Tk_c, hkv, d] fp32
+ *   cu_seqlens_k, k_pos_offset   laid out as for cpattn_fwd_chunks
+ *   workspace   >= cpattn_bwd_workspace_size_chunks(...) bytes, 256-byte aligned
+ * Other arguments as cpattn_bwd_chunk.
+ */
+cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void* const* vs,
+                                int32_t nchunks, const float* o, const void* do_,
+                                const float* lse, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const int32_t* q_pos_offset,
+                                const int32_t* k_pos_offset, int32_t nseq, int32_t hq,
+                                int32_t hkv, int32_t d, cpattn_dtype dtype, int32_t causal,
+                                float* dq, float* const* dks, float* const* dvs, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Bytes of device workspace one cpattn_bwd_chunk call needs (plans of both kernels
  * and delta [hq, Tq] fp32).  Returns 0 for invalid arguments.
  */
 size_t cpattn_bwd_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_k, int32_t hq, int32_t hkv, int32_t d);
+
+/* The same for cpattn_bwd_chunks with nchunks chunks (cu_seqlens_k [nchunks][nseq + 1]). */
+size_t cpattn_bwd_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_q,
+                                        const int32_t* cu_seqlens_k, int32_t nchunks, int32_t hq,
+                                        int32_t hkv, int32_t d);
 
 /*
  * The online-softmax merge of the pages' ring loop ("Megatron 6D parallelism

@@ -1,8 +1,9 @@
-"""GPU parity of the backward (cpattn_bwd_chunk) against the fp64 oracle's gradients.
+"""GPU parity of the backward (cpattn_bwd_chunks, cpattn_bwd_chunk) against the fp64
+oracle's gradients.
 
 The forward runs on the GPU (one launch over all chunks, giving the share's O and
-LSE), then the backward once per chunk: dq accumulates over the chunks, each call
-yields that chunk's dk and dv.  The oracle differentiates the unsplit attention of
+LSE), then the backward: one pass over all chunks, or (per_chunk) once per chunk
+with dq accumulating over the calls and each call yielding that chunk's dk and dv.  The oracle differentiates the unsplit attention of
 the share; dq is compared whole, dk / dv chunk by chunk against the oracle's rows
 of that chunk's keys.
 
@@ -61,15 +62,16 @@ def _split(rng, cu_k, ko, nchunks):
     return rows, cus, offs
 
 
-def _run(cra, q, k, v, do, cu_q, cu_k, qo, ko, causal, nchunks, rng):
-    """GPU forward over the chunks, then per-chunk backward; returns dq and full-length dk, dv."""
+def _run(cra, q, k, v, do, cu_q, cu_k, qo, ko, causal, nchunks, rng, per_chunk=False):
+    """GPU forward over the chunks, then the backward; returns dq and full-length dk, dv."""
     import torch
     rows, cus, offs = _split(rng, cu_k, ko, nchunks)
     Q, DO = dev(q, "bfloat16"), dev(do, "bfloat16")
     ks = [dev(k[r], "bfloat16") for r in rows]
     vs = [dev(v[r], "bfloat16") for r in rows]
     o, lse = cra.cpattn_fwd_chunks(Q, ks, vs, cu_q, cus, qo, offs, causal)
-    dq, dks, dvs = cra.cpattn_share_bwd(Q, ks, vs, o, lse, DO, cu_q, cus, qo, offs, causal)
+    dq, dks, dvs = cra.cpattn_share_bwd(Q, ks, vs, o, lse, DO, cu_q, cus, qo, offs, causal,
+                                        per_chunk=per_chunk)
     torch.cuda.synchronize()
     dk = np.zeros(k.shape); dv = np.zeros(v.shape)
     for c, r in enumerate(rows):
@@ -169,3 +171,29 @@ def test_backward_rejects_fp32(gpu_lib):
     with pytest.raises(gpu_lib.CpattnError) as ei:
         gpu_lib.cpattn_bwd_chunk(q, q, q, q, lse, q, [0, 4], [0, 4])
     assert ei.value.status == 2
+
+
+@pytest.mark.parametrize("per_chunk", [False, True])
+@pytest.mark.parametrize("nchunks", [1, 3, 8, 16])
+def test_backward_chunk_counts_both_schedules(gpu_lib, nchunks, per_chunk):
+    rng = np.random.default_rng(300 + nchunks)
+    q, k, v, cu_q, cu_k, qo, ko = wl.random_pack(rng, 4, 260, 16, 4, 128, dtype="bf16",
+                                                 min_len=1, k_extra=64)
+    do = wl.round_to_bf16(rng.standard_normal(q.shape, dtype=np.float32))
+    dq, dk, dv = _run(gpu_lib, q, k, v, do, cu_q, cu_k, qo, ko, True, nchunks, rng, per_chunk)
+    rq, rk, rv = attention_bwd_ref(q, k, v, do, cu_q, cu_k, qo, ko, True)
+    what = f"{nchunks} chunks, per_chunk={per_chunk}"
+    check_grad(dq, rq, "dq " + what)
+    check_grad(dk, rk, "dk " + what)
+    check_grad(dv, rv, "dv " + what)
+
+
+def test_backward_too_many_chunks_is_rejected(gpu_lib):
+    import torch
+    q = dev(np.ones((4, 2, 64), np.float32), "bfloat16")
+    o = torch.zeros((4, 2, 64), device="cuda")
+    lse = torch.zeros((2, 4), device="cuda")
+    n = gpu_lib.MAX_CHUNKS + 1
+    with pytest.raises(gpu_lib.CpattnError) as ei:
+        gpu_lib.cpattn_bwd_chunks(q, [q] * n, [q] * n, o, lse, q, [0, 4], [[0, 4]] * n)
+    assert ei.value.status == 1

@@ -307,3 +307,32 @@ def test_fwd_chunks_rejects_bad_arguments_without_a_gpu(lib):
     assert call(vs=ptrs(1 << 26, None)) == cra._binding.ERR_INVALID_ARG             # null v
     assert call(o=ctypes.c_void_p(1 << 25)) == cra._binding.ERR_INVALID_ARG         # o overlaps chunk 1's k
     assert b"overlap" in lib.cpattn_last_error()
+
+
+def test_bwd_rejects_bad_arguments_without_a_gpu(lib):
+    cu, pcu = _i32([0, 64])
+    cu2, pcu2 = _i32([0, 64, 0, 64])
+    fake = ctypes.c_void_p(4096)
+    ptrs = lambda *a: (ctypes.c_void_p * len(a))(*a)
+    ks, vs = ptrs(1 << 24, 1 << 25), ptrs(1 << 26, 1 << 27)
+    dks, dvs = ptrs(1 << 34, 1 << 35), ptrs(1 << 36, 1 << 37)
+    ws = ctypes.c_void_p(1 << 20)
+
+    def call(**kw):
+        return lib.cpattn_bwd_chunks(
+            kw.get("q", fake), kw.get("ks", ks), kw.get("vs", vs), kw.get("nch", 2),
+            ctypes.c_void_p(1 << 28), ctypes.c_void_p(1 << 29), ctypes.c_void_p(1 << 30), pcu,
+            kw.get("cuk", pcu2), None, None, 1, 4, 2, 64, kw.get("dtype", 0), 1,
+            kw.get("dq", ctypes.c_void_p(1 << 33)), kw.get("dks", dks), kw.get("dvs", dvs), ws,
+            1 << 20, None)
+
+    assert call(nch=0) == cra._binding.ERR_INVALID_ARG
+    assert call(nch=cra.MAX_CHUNKS + 1) == cra._binding.ERR_INVALID_ARG
+    assert call(dks=None) == cra._binding.ERR_INVALID_ARG
+    assert call(dtype=1) == cra._binding.ERR_UNSUPPORTED                    # fp32: forward only
+    assert call(q=ctypes.c_void_p(0)) == cra._binding.ERR_INVALID_ARG
+    assert call(dq=ctypes.c_void_p(1 << 24)) == cra._binding.ERR_INVALID_ARG  # dq overlaps k of chunk 0
+    assert call(dvs=ptrs(1 << 36, 1 << 34)) == cra._binding.ERR_INVALID_ARG  # dv aliases dk
+    assert b"overlap" in lib.cpattn_last_error()
+    assert cra.cpattn_bwd_workspace_size_chunks(1, [0, 64], [[0, 64]] * 2, 4, 2, 64) >= \
+        cra.cpattn_bwd_workspace_size(1, [0, 64], [0, 64], 4, 2, 64)
