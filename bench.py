@@ -36,6 +36,7 @@ ATTN_SOURCE = os.path.join(HERE, "context_ring_attention_amd", "csrc", "attn_fwd
 # they were taken on.  Any other pair reports traffic as null until it is profiled again.
 PROFILED_TRAFFIC = {
     ("cp4_share", "2b8e1b79d16083ab3b7717095bb764caf95067a5e79bf8180c95ba3317755a9f"): 225710736,
+    ("ctx128k_share", "2b8e1b79d16083ab3b7717095bb764caf95067a5e79bf8180c95ba3317755a9f"): 2548746465,
 }
 
 
