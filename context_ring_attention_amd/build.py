@@ -18,8 +18,11 @@ LIB = os.path.join(PKG, "libcpattn.so")
 
 SOURCES = ["api.cpp", "plan.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip",
            "merge.hip"]
-# Per-source extra flags (the bf16 kernels never produce NaN; see their header comments).
-EXTRA = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_bwd_bf16.hip": ["-fno-honor-nans"]}
+# Per-source extra flags.  The bf16 kernels never produce NaN (see their header comments).
+# The forward kernel is scheduled with the backend's iterative ILP strategy, which measured
+# faster than the default occupancy-first one for it.
+EXTRA = {"attn_fwd_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+         "attn_bwd_bf16.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are disabled for all device code.

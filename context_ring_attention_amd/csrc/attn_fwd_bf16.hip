@@ -272,6 +272,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
             if (32 + kin > lim) s1[r] = -INFINITY;
           }
         }
+        // V^T fragments of the first NH key groups, read before the softmax so that their LDS
+        // latency hides behind its VALU work (more groups only add register pressure).
+        constexpr int NH = 1;
+        bf16x8 va[NH][DT];
+#pragma unroll
+        for (int kk = 0; kk < NH; ++kk) {
+          const int row = 16 * kk + 4 * g + jr;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int c16 = 4 * dt + 2 * hh + (qq >> 1);
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(s + L::v_off(row, c16) + 8 * (qq & 1)));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(s + L::v_off(row + 8, c16) + 8 * (qq & 1)));
+            va[kk][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // ---- online softmax ----
         // P = exp2(s c - m c) as bf16 B operands (key group kk = registers 8 (kk % 2) .. +7 of
         // tile kk / 2) and this lane's sum of them.
@@ -335,12 +353,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
           const int row = 16 * kk + 4 * g + jr;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const int c16 = 4 * dt + 2 * hh + (qq >> 1);
-            const int off0 = L::v_off(row, c16) + 8 * (qq & 1);
-            const int off1 = L::v_off(row + 8, c16) + 8 * (qq & 1);
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off0));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off1));
-            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            bf16x8 a;
+            if (kk < NH) {
+              a = va[kk < NH ? kk : 0][dt];
+            } else {
+              const int c16 = 4 * dt + 2 * hh + (qq >> 1);
+              const int off0 = L::v_off(row, c16) + 8 * (qq & 1);
+              const int off1 = L::v_off(row + 8, c16) + 8 * (qq & 1);
+              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off0));
+              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off1));
+              a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], acc[dt], 0, 0, 0);
           }
         }
