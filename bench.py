@@ -35,8 +35,8 @@ ATTN_SOURCE = os.path.join(HERE, "context_ring_attention_amd", "csrc", "attn_fwd
 # (scaled by a plain-copy calibration), keyed by workload and the sha256 of the kernel source
 # they were taken on.  Any other pair reports traffic as null until it is profiled again.
 PROFILED_TRAFFIC = {
-    ("cp4_share", "2b8e1b79d16083ab3b7717095bb764caf95067a5e79bf8180c95ba3317755a9f"): 225710736,
-    ("ctx128k_share", "2b8e1b79d16083ab3b7717095bb764caf95067a5e79bf8180c95ba3317755a9f"): 2548746465,
+    ("cp4_share", "d10ef45935ad77971220ad11ea0fddab51b8812736092d9dafd710da2197323a"): 223390240,
+    ("ctx128k_share", "d10ef45935ad77971220ad11ea0fddab51b8812736092d9dafd710da2197323a"): 3136331797,
 }
 
 
@@ -49,6 +49,14 @@ def visible_pairs(cu_q, cu_k, q_off, k_off) -> int:
         for_rows = np.clip(d0 + 1 + np.arange(nq, dtype=np.int64), 0, nk)
         total += int(for_rows.sum())
     return total
+
+
+def pack_words(lengths) -> str:
+    """'one 131,072-token sequence' or 'a 16,384-token THD pack of 2 sequences'."""
+    total = int(sum(lengths))
+    if len(lengths) == 1:
+        return f"one {total:,}-token sequence"
+    return f"a {total:,}-token THD pack of {len(lengths)} sequences"
 
 
 def cpu_baseline(w, g, budget_rows: int = 4096):
@@ -267,11 +275,12 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name} (seed {w.seed}): last CP4 rank of a 16,384-token THD "
-                               f"pack, local Q {tq} tokens in {len(cu_q) - 1} sequences, "
-                               f"{nch} KV chunks of {int(cu_ks[0][-1])} tokens, "
-                               f"{w.hq}/{w.hkv} heads, D={w.d}, causal",
-                   "global_batch": 16384, "seq_len": int(max(w.lengths)), "parallelism": "cp4-share"},
+        "config": {"workload": f"{w.name} (seed {w.seed}): last CP{nch} rank of "
+                               f"{pack_words(w.lengths)}, local Q {tq} tokens in "
+                               f"{len(cu_q) - 1} sequences, {nch} KV chunks of "
+                               f"{int(cu_ks[0][-1])} tokens, {w.hq}/{w.hkv} heads, D={w.d}, causal",
+                   "global_batch": int(sum(w.lengths)), "seq_len": int(max(w.lengths)),
+                   "parallelism": f"cp{nch}-share"},
         "mfma_util": round(value / BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
