@@ -312,7 +312,23 @@ def main() -> int:
         torch.cuda.synchronize()
         del evict
         result["copy_calibration_bytes"] = {"read": n * 4, "written": n * 4}
+    # The Dynamic-CP host scheduler on the Dynamic-CP mini-batch (65,536 tokens, lognormal
+    # lengths) for DP x CP = 8 ranks under the CP4 per-rank limit of 4,096 tokens.
+    dcp_lens = wl.lengths_for("dcp_mixed", args.seed)
+    reps = 200
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        sched = cra.cpattn_dcp_schedule(dcp_lens, 8, 4096)
+    dcp_us = (time.perf_counter() - t0) / reps * 1e6
+    result["dcp_schedule"] = {"samples": len(dcp_lens), "tokens": int(sum(dcp_lens)), "world": 8,
+                              "max_seqlen_per_rank": 4096, "micro_batches": sched["n_micro_batches"],
+                              "host_us_per_call": round(dcp_us, 1)}
     if not args.no_cpu_baseline:
+        from oracle.dcp import dcp_schedule_ref
+        t0 = time.perf_counter()
+        for _ in range(20):
+            dcp_schedule_ref(dcp_lens, 8, 4096)
+        result["dcp_schedule"]["oracle_host_us_per_call"] = round((time.perf_counter() - t0) / 20 * 1e6, 1)
         cb = cpu_baseline(w, g)
         cb["value"] = float(f"{cb['value']:.4g}")
         cb.pop("seconds", None)

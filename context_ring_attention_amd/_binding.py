@@ -26,7 +26,8 @@ EXPORTED = ("cpattn_workspace_size", "cpattn_workspace_size_chunks", "cpattn_fwd
             "cpattn_fwd_chunk_accum", "cpattn_fwd_chunks", "cpattn_bwd_chunk", "cpattn_bwd_chunks",
             "cpattn_bwd_workspace_size", "cpattn_bwd_workspace_size_chunks", "cpattn_merge",
             "cpattn_status_string",
-            "cpattn_last_error", "cpattn_plan_build", "cpattn_plan_build_chunks")
+            "cpattn_last_error", "cpattn_plan_build", "cpattn_plan_build_chunks",
+            "cpattn_dcp_schedule")
 MAX_CHUNKS = 16  # CPATTN_MAX_CHUNKS
 
 
@@ -108,6 +109,9 @@ def load(path: str = LIB_PATH):
     lib.cpattn_plan_build_chunks.argtypes = [_I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
                                              c_int32, c_int32, c_int, c_int32, c_void_p, c_size_t,
                                              POINTER(PlanInfo)]
+    lib.cpattn_dcp_schedule.restype = c_int
+    lib.cpattn_dcp_schedule.argtypes = [_I32P, c_int32, c_int32, c_int32, _I32P, _I32P, _I32P, _I32P,
+                                        _I32P]
     _lib = lib
     return lib
 
@@ -204,6 +208,23 @@ def cpattn_plan_build(cu_seqlens_q, cu_seqlens_k, q_pos_offset=None, k_pos_offse
     _check(lib.cpattn_plan_build(pq, pk, pqo, pko, nseq, hq, hkv, d, dtype, int(causal),
                                  c_void_p(entries.ctypes.data), entries.nbytes, ctypes.byref(info)))
     return entries, {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+
+
+def cpattn_dcp_schedule(lengths, world: int, max_seqlen_per_rank: int) -> dict:
+    """Dynamic CP schedule of a mini-batch (host only): per-sample cp_size, micro_batch,
+    group_rank (first rank of its CP group) and slot (position in the group's pack) as int32
+    arrays, and n_micro_batches."""
+    n = len(lengths)
+    arr, ptr = _host_i32(lengths, n, "lengths")
+    outs = {k: np.zeros(max(n, 1), dtype=np.int32) for k in ("cp_size", "micro_batch", "group_rank", "slot")}
+    nmb = np.zeros(1, dtype=np.int32)
+    p = lambda a: a.ctypes.data_as(_I32P)
+    _check(load().cpattn_dcp_schedule(ptr, n, int(world), int(max_seqlen_per_rank), p(outs["cp_size"]),
+                                      p(outs["micro_batch"]), p(outs["group_rank"]), p(outs["slot"]),
+                                      p(nmb)))
+    res = {k: v[:n] for k, v in outs.items()}
+    res["n_micro_batches"] = int(nmb[0])
+    return res
 
 
 def cpattn_workspace_size_chunks(nseq: int, cu_seqlens_q, hq: int, hkv: int, d: int,

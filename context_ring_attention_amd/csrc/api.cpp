@@ -161,6 +161,15 @@ cpattn_status cpattn_plan_build_chunks(const int32_t* cu_seqlens_q, const int32_
   return CPATTN_OK;
 }
 
+cpattn_status cpattn_dcp_schedule(const int32_t* lengths, int32_t n, int32_t world,
+                                  int32_t max_seqlen_per_rank, int32_t* cp_size,
+                                  int32_t* micro_batch, int32_t* group_rank, int32_t* slot,
+                                  int32_t* n_micro_batches) {
+  clear_error();
+  return dcp_schedule(lengths, n, world, max_seqlen_per_rank, cp_size, micro_batch, group_rank,
+                      slot, n_micro_batches);
+}
+
 cpattn_status cpattn_plan_build(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                 const int32_t* q_pos_offset, const int32_t* k_pos_offset,
                                 int32_t nseq, int32_t hq, int32_t hkv, int32_t d,

@@ -85,6 +85,11 @@ struct ChunkPtrs {
 
 cpattn_status set_error(cpattn_status s, const char* fmt, ...);
 
+// The Dynamic CP scheduler behind cpattn_dcp_schedule (dcp.cpp).
+cpattn_status dcp_schedule(const int32_t* lengths, int32_t n, int32_t world, int32_t limit,
+                           int32_t* cp_size, int32_t* micro_batch, int32_t* group_rank,
+                           int32_t* slot, int32_t* n_micro_batches);
+
 // Kernel launchers (defined in the .hip files).  They assume validated input.
 // plan holds n_tiles * nchunks entries (tile-major); accumulate folds the result
 // into (o, lse) instead of overwriting them.

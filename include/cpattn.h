@@ -303,6 +303,41 @@ cpattn_status cpattn_plan_build_chunks(const int32_t* cu_seqlens_q, const int32_
                                        cpattn_plan_entry* plan, size_t plan_bytes,
                                        cpattn_plan_info* info);
 
+/* -------------------------------------------------------------------------
+ * Dynamic Context Parallelism scheduler (host only, no device work).
+ *
+ * Chooses a CP group size for every sample of a mini-batch and places the
+ * samples into micro-batches of CP groups, under the constraints of the verl
+ * page "Dynamic Context Parallelism": every DP x CP rank sees the whole
+ * mini-batch; a per-rank token limit max_seqlen_per_dp_cp_rank (e.g. 16384 / 4
+ * = 4096 for a static CP4 run with a 16,384-token budget); CP groups are the
+ * power-of-two subgroups of the `world` = DP x CP ranks plus the full group, and
+ * world must be an even integer of at least two.  The pages do not print the
+ * assignment rule; this one (see csrc/dcp.cpp) is:
+ *   - cp_size[i] = the smallest allowed group size g with ceil(L_i / g) <= limit;
+ *   - sample i is split into g contiguous pieces of ceil(L_i / g) tokens (the
+ *     last one the remainder); rank group_rank[i] + r holds piece r;
+ *   - samples are placed in decreasing (g, L) order, first fit over the
+ *     micro-batches: into an existing group of size g if every rank stays within
+ *     the limit, else into a new group at the lowest free aligned rank (a
+ *     multiple of g; the full group at rank 0), else into a new micro-batch.
+ * Every rank of a micro-batch belongs to at most one group.
+ *
+ *   lengths        host int32 [n], >= 0
+ *   cp_size        host int32 [n] out: group size of sample i
+ *   micro_batch    host int32 [n] out: micro-batch of sample i (0-based)
+ *   group_rank     host int32 [n] out: first rank of sample i's group
+ *   slot           host int32 [n] out: position of sample i in its group's THD pack
+ *   n_micro_batches host int32 out
+ * Returns CPATTN_ERR_INVALID_ARG (and writes nothing meaningful) for an odd or
+ * too small world, a limit < 1, a negative length, or a sample longer than
+ * world x limit.  Deterministic; thread-safe.
+ * ------------------------------------------------------------------------- */
+cpattn_status cpattn_dcp_schedule(const int32_t* lengths, int32_t n, int32_t world,
+                                  int32_t max_seqlen_per_rank, int32_t* cp_size,
+                                  int32_t* micro_batch, int32_t* group_rank, int32_t* slot,
+                                  int32_t* n_micro_batches);
+
 #ifdef __cplusplus
 }
 #endif
