@@ -306,7 +306,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct BwdLayout {
   int64_t n_q, n_k;        // tiles of the query plan and of the key plan
-  size_t key_plan_at, delta_at, plan_bytes, total;
+  size_t key_plan_at, delta_at, lse2_at, plan_bytes, total;
 };
 
 BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq) {
@@ -316,7 +316,8 @@ BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq) {
   l.key_plan_at = align256(size_t(n_q) * sizeof(cpattn_plan_entry));
   l.plan_bytes = l.key_plan_at + size_t(n_k) * sizeof(cpattn_plan_entry);
   l.delta_at = align256(l.plan_bytes);
-  l.total = std::max<size_t>(256, l.delta_at + size_t(tq) * hq * sizeof(float));
+  l.lse2_at = align256(l.delta_at + size_t(tq) * hq * sizeof(float));
+  l.total = std::max<size_t>(256, l.lse2_at + size_t(tq) * hq * sizeof(float));
   return l;
 }
 }  // namespace
@@ -424,6 +425,7 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
   const auto* qplan = reinterpret_cast<const cpattn_plan_entry*>(ws);
   const auto* kplan = reinterpret_cast<const KeyTile*>(ws + lay.key_plan_at);
   float* delta = reinterpret_cast<float*>(ws + lay.delta_at);
+  float* lse2 = reinterpret_cast<float*>(ws + lay.lse2_at);
   ChunkPtrs<__bf16> kv{};
   ChunkPtrs<float> dkv{};
   for (int32_t c = 0; c < nchunks; ++c) {
@@ -432,12 +434,12 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
     dkv.k[c] = dks[c];
     dkv.v[c] = dvs[c];
   }
-  hipError_t err = launch_bwd_delta(do_, o, int(tq), hq, d, delta, stream);
+  hipError_t err = launch_bwd_delta(do_, o, lse, int(tq), hq, d, delta, lse2, stream);
   if (err == hipSuccess)
     err = launch_bwd_dq(q, kv, nchunks, do_, lse, delta, qplan, int(n_qt), head_groups,
                         g.heads_per_tile, hq, hkv, d, int(tq), dq, stream);
   if (err == hipSuccess)
-    err = launch_bwd_dkdv(q, kv, do_, lse, delta, kplan, int(lay.n_k), hq, hkv, d, int(tq), dkv,
+    err = launch_bwd_dkdv(q, kv, do_, lse2, delta, kplan, int(lay.n_k), hq, hkv, d, int(tq), dkv,
                           stream);
   if (err != hipSuccess)
     return set_error(CPATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));

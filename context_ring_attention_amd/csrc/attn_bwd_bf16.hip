@@ -6,7 +6,8 @@
 // exactly that LSE), dP = dO V^T and dS = P * (dP - delta), delta = rowsum(dO * O):
 //   dQ += dS K / sqrt(D),   dK += dS^T Q / sqrt(D),   dV += P^T dO.
 // Three kernels, no atomics (results are deterministic):
-//   bwd_delta   delta [hq, Tq] = rowsum(dO * O), HBM-bound;
+//   bwd_delta   delta [hq, Tq] = rowsum(dO * O), HBM-bound, and the LSE in log2 units
+//               (+inf for rows with no visible key) for bwd_dkdv;
 //   bwd_dq      query-stationary, the forward's tiling and its walk over the KV
 //               chunks: per 64-key block S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, then
 //               dQ^T += K^T dS^T; dQ is written once per launch;
@@ -15,7 +16,9 @@
 //               the query tokens that see them, 64 at a time, for every query head
 //               of the group: S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P,
 //               dK^T += Q^T dS.  One launch covers the key tiles of every chunk,
-//               longest first.
+//               longest first.  Query blocks that see every key of a wave (all but
+//               the causal diagonal and ragged ends) take a copy of the step without
+//               the per-element mask.
 // Matrix-core mapping: every product is a v_mfma_f32_32x32x16_bf16 whose result
 // keeps one column index per lane (lane % 32) and 16 row indices per lane, like the
 // forward's S^T tile; the probability-like results (P, dS) are rounded to bf16 and
@@ -26,6 +29,8 @@
 //
 // This file is compiled with -fno-honor-nans: rows with no visible key use an
 // effective LSE of +inf, so every exponent is finite or -inf and no NaN arises.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace cpattn {
@@ -149,12 +154,16 @@ __device__ __forceinline__ void pack_b(const f32x16& t0, const f32x16& t1, bf16x
 #endif  // __HIP_DEVICE_COMPILE__
 
 // ---------------------------------------------------------------------------
-// delta[h][t] = sum_d dO[t, h, d] * O[t, h, d]: 16 lanes per (t, h) row.
+// delta[h][t] = sum_d dO[t, h, d] * O[t, h, d]: 16 lanes per (t, h) row; alongside, the row's
+// LSE in log2 units, lse2[h][t] = LSE * log2(e), or +inf for a row with no visible key, so
+// that P = exp2(S * scale * log2(e) - lse2) is one FMA and one exp2 (and 0 for such rows).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const __bf16* __restrict__ dout,
-                                                             const float* __restrict__ o, int tq,
-                                                             int hq, float* __restrict__ delta) {
+                                                             const float* __restrict__ o,
+                                                             const float* __restrict__ lse, int tq,
+                                                             int hq, float* __restrict__ delta,
+                                                             float* __restrict__ lse2) {
   constexpr int EL = D / 16;  // elements per lane
   const int64_t rows = int64_t(tq) * hq;
   const int sub = threadIdx.x & 15;
@@ -180,6 +189,8 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const __bf16* __res
       const int64_t t = r / hq;
       const int h = int(r - t * hq);
       delta[int64_t(h) * tq + t] = acc;
+      const float l = lse[int64_t(h) * tq + t];
+      lse2[int64_t(h) * tq + t] = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
     }
   }
 }
@@ -317,14 +328,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const ChunkPtrs<__bf16> kv, const __bf16* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ lse2, const float* __restrict__ delta,
     const KeyTile* __restrict__ plan, int hq, int hkv, int tq, float scale, float scale_log2,
     const ChunkPtrs<float> dkv) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = Tile<D>;
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
-  constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, LSE[64], delta[64]
+  constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, lse2[64], delta[64]
   __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
 
   const int tid = threadIdx.x;
@@ -371,8 +382,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     char* s = smem + stage * kStage;
     load_tile<D, true>(q, first, h, hq, left, s, wave, lane);
     load_tile<D, true>(dout, first, h, hq, left, s + T::kBytes, wave, lane);
-    if (wave < 2) {  // LSE (wave 0) and delta (wave 1) of the block's 64 rows, 4 bytes per lane
-      const float* src = (wave == 0 ? lse : delta) + int64_t(h) * tq + first;
+    if (wave < 2) {  // lse2 (wave 0) and delta (wave 1) of the block's 64 rows, 4 bytes per lane
+      const float* src = (wave == 0 ? lse2 : delta) + int64_t(h) * tq + first;
       const __amdgpu_buffer_rsrc_t r = make_rsrc(src, left * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(s + 2 * T::kBytes + 256 * wave), 4,
                                                lane * 4, 0, 0, 0);
@@ -390,38 +401,55 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const char* dt_ = qt + T::kBytes;
     const float* lse_s = reinterpret_cast<const float*>(qt + 2 * T::kBytes);
     const float* del_s = lse_s + 64;
-    f32x16 s0, s1, p0, p1;
-    rows_product<D, true>(qt, kf, n, g, s0, s1);   // S = Q K^T   (rows: tokens)
-    rows_product<D, true>(dt_, vf, n, g, p0, p1);  // dP = dO V^T
     // Query (within the sequence) of register r of tile tt: t_first + 64 j + 32 tt + 8 (r / 4)
-    // + 4 g + r % 4; visible iff it is < k_len and >= delta + key.
+    // + 4 g + r % 4; visible iff it is < q_len and >= delta + key.  A block whose every query
+    // sees every key of this wave (the common case) skips the per-element test.  The two
+    // cases are separate copies of the whole step, so no branch separates the products from
+    // the reads of their results.
     const int tb = t_first + j * QB + 4 * g;
     const int lo = pe.delta + key, hi_excl = pe.q_len;
-    bf16x8 pb[4], db[4];
-    {
+    const int blk0 = t_first + j * QB;
+    const bool full = 32 * wave + 31 < pe.nrows && blk0 >= pe.delta + 32 * wave + 31 &&
+                      blk0 + QB <= pe.q_len;
+    auto step_body = [&](auto masked) {
+      f32x16 s0, s1, p0, p1;
+      rows_product<D, true>(qt, kf, n, g, s0, s1);   // S = Q K^T   (rows: tokens)
+      rows_product<D, true>(dt_, vf, n, g, p0, p1);  // dP = dO V^T
+      bf16x8 pb[4], db[4];
       f32x16 ps0, ps1;
+      // Registers 4 i .. 4 i + 3 of tile tt hold rows 32 tt + 8 i + 4 g .. + 3: their lse2 and
+      // delta are one 16-byte LDS read each.  P = exp2(S c - lse2), dS = P (dP - delta).
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ti = 8 * (r >> 2) + (r & 3) + 4 * g;         // row within the 64-row block
-        const int t0 = tb + 8 * (r >> 2) + (r & 3), t1 = t0 + 32;
-        const float l0 = lse_s[ti], l1 = lse_s[32 + ti];
-        const float le0 = l0 == -INFINITY ? INFINITY : l0 * 1.4426950408889634f;
-        const float le1 = l1 == -INFINITY ? INFINITY : l1 * 1.4426950408889634f;
-        const bool v0 = key_ok && t0 >= lo && t0 < hi_excl;
-        const bool v1 = key_ok && t1 >= lo && t1 < hi_excl;
-        const float e0 = v0 ? __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -le0)) : 0.f;
-        const float e1 = v1 ? __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -le1)) : 0.f;
-        ps0[r] = e0;
-        ps1[r] = e1;
-        s0[r] = e0 * (p0[r] - del_s[ti]);                      // dS
-        s1[r] = e1 * (p1[r] - del_s[32 + ti]);
+      for (int i = 0; i < 4; ++i) {
+        const float4 l0 = *reinterpret_cast<const float4*>(lse_s + 8 * i + 4 * g);
+        const float4 l1 = *reinterpret_cast<const float4*>(lse_s + 32 + 8 * i + 4 * g);
+        const float4 d0 = *reinterpret_cast<const float4*>(del_s + 8 * i + 4 * g);
+        const float4 d1 = *reinterpret_cast<const float4*>(del_s + 32 + 8 * i + 4 * g);
+        const float la[4] = {l0.x, l0.y, l0.z, l0.w}, lb[4] = {l1.x, l1.y, l1.z, l1.w};
+        const float da[4] = {d0.x, d0.y, d0.z, d0.w}, dbv[4] = {d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int r = 4 * i + k4;
+          float e0 = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -la[k4]));
+          float e1 = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -lb[k4]));
+          if (decltype(masked)::value) {
+            const int t0 = tb + 8 * i + k4, t1 = t0 + 32;
+            e0 = key_ok && t0 >= lo && t0 < hi_excl ? e0 : 0.f;
+            e1 = key_ok && t1 >= lo && t1 < hi_excl ? e1 : 0.f;
+          }
+          ps0[r] = e0;
+          ps1[r] = e1;
+          s0[r] = e0 * (p0[r] - da[k4]);                          // dS
+          s1[r] = e1 * (p1[r] - dbv[k4]);
+        }
       }
       pack_b(ps0, ps1, pb);
       pack_b(s0, s1, db);
-    }
-    transposed_product<D>(dt_, pb, n, g, dvt);   // dV^T += dO^T P
-    transposed_product<D>(qt, db, n, g, dkt);    // dK^T += Q^T dS
-    (void)j;
+      transposed_product<D>(dt_, pb, n, g, dvt);   // dV^T += dO^T P
+      transposed_product<D>(qt, db, n, g, dkt);    // dK^T += Q^T dS
+    };
+    if (full) step_body(std::false_type{});
+    else step_body(std::true_type{});
   }
 
   if (key_ok) {
@@ -446,8 +474,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
 }  // namespace
 
-hipError_t launch_bwd_delta(const void* do_, const float* o, int tq, int hq, int d, float* delta,
-                            hipStream_t stream) {
+hipError_t launch_bwd_delta(const void* do_, const float* o, const float* lse, int tq, int hq,
+                            int d, float* delta, float* lse2, hipStream_t stream) {
   const int64_t rows = int64_t(tq) * hq;
   if (rows == 0) return hipSuccess;
   int64_t blocks = (rows * 16 + kThreads - 1) / kThreads;
@@ -455,10 +483,10 @@ hipError_t launch_bwd_delta(const void* do_, const float* o, int tq, int hq, int
   const auto* db = static_cast<const __bf16*>(do_);
   if (d == 128) {
     hipLaunchKernelGGL(bwd_delta_kernel<128>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, db, o,
-                       tq, hq, delta);
+                       lse, tq, hq, delta, lse2);
   } else if (d == 64) {
     hipLaunchKernelGGL(bwd_delta_kernel<64>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, db, o,
-                       tq, hq, delta);
+                       lse, tq, hq, delta, lse2);
   } else {
     return hipErrorInvalidValue;
   }
@@ -485,7 +513,7 @@ hipError_t launch_bwd_dq(const void* q, const ChunkPtrs<__bf16>& kv, int nchunks
 }
 
 hipError_t launch_bwd_dkdv(const void* q, const ChunkPtrs<__bf16>& kv, const void* do_,
-                           const float* lse, const float* delta, const KeyTile* plan, int n_tiles,
+                           const float* lse2, const float* delta, const KeyTile* plan, int n_tiles,
                            int hq, int hkv, int d, int tq, const ChunkPtrs<float>& dkv,
                            hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
@@ -494,7 +522,7 @@ hipError_t launch_bwd_dkdv(const void* q, const ChunkPtrs<__bf16>& kv, const voi
   const float scale_log2 = scale * 1.4426950408889634f;
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const __bf16*>(q), kv,
-                       static_cast<const __bf16*>(do_), lse, delta, plan, hq, hkv, tq, scale,
+                       static_cast<const __bf16*>(do_), lse2, delta, plan, hq, hkv, tq, scale,
                        scale_log2, dkv);
   };
   if (d == 128) launch(bwd_dkdv_kernel<128>);

@@ -103,14 +103,14 @@ hipError_t launch_attn_fwd_f32(const float* q, const ChunkPtrs<float>& kv, int n
                                hipStream_t stream);
 // Backward launchers: delta = rowsum(dO * O) into delta [hq, tq]; dQ over the query plan
 // (tile-major over nchunks chunks, as the forward's); dK, dV over the key plan.
-hipError_t launch_bwd_delta(const void* do_, const float* o, int tq, int hq, int d, float* delta,
-                            hipStream_t stream);
+hipError_t launch_bwd_delta(const void* do_, const float* o, const float* lse, int tq, int hq,
+                            int d, float* delta, float* lse2, hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const ChunkPtrs<__bf16>& kv, int nchunks, const void* do_,
                          const float* lse, const float* delta, const cpattn_plan_entry* plan,
                          int n_tiles, int head_groups, int heads_per_tile, int hq, int hkv, int d,
                          int tq, float* dq, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const void* q, const ChunkPtrs<__bf16>& kv, const void* do_,
-                           const float* lse, const float* delta, const KeyTile* plan, int n_tiles,
+                           const float* lse2, const float* delta, const KeyTile* plan, int n_tiles,
                            int hq, int hkv, int d, int tq, const ChunkPtrs<float>& dkv,
                            hipStream_t stream);
 hipError_t launch_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,

@@ -174,7 +174,7 @@ cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void
  *   dq        device [Tq, hq, d] fp32; dk, dv device [Tk, hkv, d] fp32   (read and written)
  *   metadata  as cpattn_fwd_chunk (host); dtype must be CPATTN_BF16; d in {64, 128}
  *   workspace device, >= cpattn_bwd_workspace_size(...) bytes, 256-byte aligned; it holds
- *             the plans and delta until the kernels have run
+ *             the plans, delta and the log2-scaled LSE until the kernels have run
  * Rows whose LSE is -inf (no visible key in the share) contribute nothing.  No output may
  * overlap an input or another output.  Returns CPATTN_OK, or an error code with nothing
  * enqueued (CPATTN_ERR_UNSUPPORTED for fp32 inputs).
@@ -209,8 +209,8 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Bytes of device workspace one cpattn_bwd_chunk call needs (plans of both kernels
- * and delta [hq, Tq] fp32).  Returns 0 for invalid arguments.
+ * Bytes of device workspace one cpattn_bwd_chunk call needs (plans of both kernels,
+ * delta [hq, Tq] and the LSE in log2 units [hq, Tq], fp32).  Returns 0 for invalid arguments.
  */
 size_t cpattn_bwd_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_k, int32_t hq, int32_t hkv, int32_t d);
