@@ -16,9 +16,10 @@
 //               the query tokens that see them, 64 at a time, for every query head
 //               of the group: S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P,
 //               dK^T += Q^T dS.  One launch covers the key tiles of every chunk,
-//               longest first.  Query blocks that see every key of a wave (all but
-//               the causal diagonal and ragged ends) take a copy of the step without
-//               the per-element mask.
+//               longest first.  Query blocks that see every key of the tile (all but
+//               the causal diagonal and the ragged end) run in a loop of their own over
+//               a copy of the step without the per-element mask; with one loop body per
+//               case the accumulators stay in the matrix-core registers.
 // Matrix-core mapping: every product is a v_mfma_f32_32x32x16_bf16 whose result
 // keeps one column index per lane (lane % 32) and 16 row indices per lane, like the
 // forward's S^T tile; the probability-like results (P, dS) are rounded to bf16 and
@@ -390,8 +391,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
   };
 
-  if (total > 0) issue(0, 0);
-  for (int step = 0; step < total; ++step) {
+  // Query blocks that every query of the tile's 128 keys sees (all but the causal diagonal
+  // and the ragged end): j in [j_full0, j_full1) of every head; the steps of a head run in
+  // three loops (masked, unmasked, masked) so each loop body is one straight copy of the step.
+  const bool tile_full = pe.nrows == kBwdKeysPerTile;
+  const int j_full0 = tile_full ? min(nblk, max(0, (pe.delta + kBwdKeysPerTile - 1 - t_first + QB - 1) / QB)) : nblk;
+  const int j_full1 = tile_full ? max(j_full0, min(nblk, (pe.q_len - t_first) / QB)) : nblk;
+  auto run_step = [&](int step, auto masked) {
     const int stage = step & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -402,54 +408,52 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const float* lse_s = reinterpret_cast<const float*>(qt + 2 * T::kBytes);
     const float* del_s = lse_s + 64;
     // Query (within the sequence) of register r of tile tt: t_first + 64 j + 32 tt + 8 (r / 4)
-    // + 4 g + r % 4; visible iff it is < q_len and >= delta + key.  A block whose every query
-    // sees every key of this wave (the common case) skips the per-element test.  The two
-    // cases are separate copies of the whole step, so no branch separates the products from
-    // the reads of their results.
+    // + 4 g + r % 4; visible iff it is < q_len and >= delta + key.
     const int tb = t_first + j * QB + 4 * g;
     const int lo = pe.delta + key, hi_excl = pe.q_len;
-    const int blk0 = t_first + j * QB;
-    const bool full = 32 * wave + 31 < pe.nrows && blk0 >= pe.delta + 32 * wave + 31 &&
-                      blk0 + QB <= pe.q_len;
-    auto step_body = [&](auto masked) {
-      f32x16 s0, s1, p0, p1;
-      rows_product<D, true>(qt, kf, n, g, s0, s1);   // S = Q K^T   (rows: tokens)
-      rows_product<D, true>(dt_, vf, n, g, p0, p1);  // dP = dO V^T
-      bf16x8 pb[4], db[4];
-      f32x16 ps0, ps1;
-      // Registers 4 i .. 4 i + 3 of tile tt hold rows 32 tt + 8 i + 4 g .. + 3: their lse2 and
-      // delta are one 16-byte LDS read each.  P = exp2(S c - lse2), dS = P (dP - delta).
+    f32x16 s0, s1, p0, p1;
+    rows_product<D, true>(qt, kf, n, g, s0, s1);   // S = Q K^T   (rows: tokens)
+    rows_product<D, true>(dt_, vf, n, g, p0, p1);  // dP = dO V^T
+    bf16x8 pb[4], db[4];
+    f32x16 ps0, ps1;
+    // Registers 4 i .. 4 i + 3 of tile tt hold rows 32 tt + 8 i + 4 g .. + 3: their lse2 and
+    // delta are one 16-byte LDS read each.  P = exp2(S c - lse2), dS = P (dP - delta).
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 l0 = *reinterpret_cast<const float4*>(lse_s + 8 * i + 4 * g);
-        const float4 l1 = *reinterpret_cast<const float4*>(lse_s + 32 + 8 * i + 4 * g);
-        const float4 d0 = *reinterpret_cast<const float4*>(del_s + 8 * i + 4 * g);
-        const float4 d1 = *reinterpret_cast<const float4*>(del_s + 32 + 8 * i + 4 * g);
-        const float la[4] = {l0.x, l0.y, l0.z, l0.w}, lb[4] = {l1.x, l1.y, l1.z, l1.w};
-        const float da[4] = {d0.x, d0.y, d0.z, d0.w}, dbv[4] = {d1.x, d1.y, d1.z, d1.w};
+    for (int i = 0; i < 4; ++i) {
+      const float4 l0 = *reinterpret_cast<const float4*>(lse_s + 8 * i + 4 * g);
+      const float4 l1 = *reinterpret_cast<const float4*>(lse_s + 32 + 8 * i + 4 * g);
+      const float4 d0 = *reinterpret_cast<const float4*>(del_s + 8 * i + 4 * g);
+      const float4 d1 = *reinterpret_cast<const float4*>(del_s + 32 + 8 * i + 4 * g);
+      const float la[4] = {l0.x, l0.y, l0.z, l0.w}, lb[4] = {l1.x, l1.y, l1.z, l1.w};
+      const float da[4] = {d0.x, d0.y, d0.z, d0.w}, dbv[4] = {d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const int r = 4 * i + k4;
-          float e0 = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -la[k4]));
-          float e1 = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -lb[k4]));
-          if (decltype(masked)::value) {
-            const int t0 = tb + 8 * i + k4, t1 = t0 + 32;
-            e0 = key_ok && t0 >= lo && t0 < hi_excl ? e0 : 0.f;
-            e1 = key_ok && t1 >= lo && t1 < hi_excl ? e1 : 0.f;
-          }
-          ps0[r] = e0;
-          ps1[r] = e1;
-          s0[r] = e0 * (p0[r] - da[k4]);                          // dS
-          s1[r] = e1 * (p1[r] - dbv[k4]);
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int r = 4 * i + k4;
+        float e0 = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -la[k4]));
+        float e1 = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -lb[k4]));
+        if (decltype(masked)::value) {
+          const int t0 = tb + 8 * i + k4, t1 = t0 + 32;
+          e0 = key_ok && t0 >= lo && t0 < hi_excl ? e0 : 0.f;
+          e1 = key_ok && t1 >= lo && t1 < hi_excl ? e1 : 0.f;
         }
+        ps0[r] = e0;
+        ps1[r] = e1;
+        s0[r] = e0 * (p0[r] - da[k4]);                            // dS
+        s1[r] = e1 * (p1[r] - dbv[k4]);
       }
-      pack_b(ps0, ps1, pb);
-      pack_b(s0, s1, db);
-      transposed_product<D>(dt_, pb, n, g, dvt);   // dV^T += dO^T P
-      transposed_product<D>(qt, db, n, g, dkt);    // dK^T += Q^T dS
-    };
-    if (full) step_body(std::false_type{});
-    else step_body(std::true_type{});
+    }
+    pack_b(ps0, ps1, pb);
+    pack_b(s0, s1, db);
+    transposed_product<D>(dt_, pb, n, g, dvt);   // dV^T += dO^T P
+    transposed_product<D>(qt, db, n, g, dkt);    // dK^T += Q^T dS
+  };
+
+  if (total > 0) issue(0, 0);
+  for (int hi = 0; hi < group; ++hi) {
+    const int base = hi * nblk;
+    for (int j = 0; j < j_full0; ++j) run_step(base + j, std::true_type{});
+    for (int j = j_full0; j < j_full1; ++j) run_step(base + j, std::false_type{});
+    for (int j = j_full1; j < nblk; ++j) run_step(base + j, std::true_type{});
   }
 
   if (key_ok) {
