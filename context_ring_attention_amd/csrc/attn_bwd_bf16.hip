@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       nfull_w = min(min(pe.k_len / BN, max(0, pe.delta + tok0 + 1) / BN), nblk_w);
     }
     const int nblk = pe.cost;
-    for (int j = 0; j < nblk; ++j, stage ^= 1) {
+    auto run_block = [&](int j, auto masked) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (j + 1 < nblk) issue(c, j + 1, stage ^ 1);
@@ -287,14 +287,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         f32x16 s0, s1, p0, p1;
         rows_product<D, true>(kt, qf, n, g, s0, s1);        // S^T = K Q^T
         rows_product<D, false>(vt, dof, n, g, p0, p1);      // dP^T = V dO^T
-        const int lim = (j >= nfull_w) ? min(pe.k_len - 1, pe.delta + tok0 + n) - j * BN - 4 * g
-                                       : BN;
+        const int lim = (decltype(masked)::value && j >= nfull_w)
+                            ? min(pe.k_len - 1, pe.delta + tok0 + n) - j * BN - 4 * g
+                            : BN;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kin = 8 * (r >> 2) + (r & 3);
-          const float e0 = kin > lim ? 0.f : __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -lse_eff));
-          const float e1 =
-              32 + kin > lim ? 0.f : __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -lse_eff));
+          float e0 = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -lse_eff));
+          float e1 = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -lse_eff));
+          if (decltype(masked)::value) {
+            e0 = kin > lim ? 0.f : e0;
+            e1 = 32 + kin > lim ? 0.f : e1;
+          }
           s0[r] = e0 * (p0[r] - delta_row);                  // dS^T
           s1[r] = e1 * (p1[r] - delta_row);
         }
@@ -302,7 +306,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         pack_b(s0, s1, dsb);
         transposed_product<D>(kt, dsb, n, g, acc);           // dQ^T += K^T dS^T
       }
-    }
+      stage ^= 1;
+    };
+    // Blocks below every wave's diagonal (the first wave's unmasked count bounds the others')
+    // run a copy of the step without the mask, in a loop of their own.
+    const int nfull_tile =
+        min(min(pe.k_len / BN, max(0, pe.delta + 1) / BN), nblk);
+    for (int j = 0; j < nfull_tile; ++j) run_block(j, std::false_type{});
+    for (int j = nfull_tile; j < nblk; ++j) run_block(j, std::true_type{});
     c = cn;
   }
 
