@@ -2,7 +2,7 @@
 """Benchmark: one CP4 rank's share of a 16,384-token packed budget on one MI355X.
 
 A step is one pass of the whole per-rank hot path on the share's inputs (already
-resident in HBM): host planning, plan upload and ONE cpattn_fwd_chunks launch that
+resident in HBM): host planning (into pinned memory the kernel reads) and ONE cpattn_fwd_chunks launch that
 walks every KV chunk of the share with the online softmax carried across chunks
 (the ring loop's merges done in registers).  `value` is the share's algorithmic
 causal FLOPs (4 * D * Hq per visible query/key pair) divided by the step time.
@@ -288,7 +288,7 @@ def main() -> int:
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)",
                      "algorithmic_bytes_per_launch": attn_bytes,
                      "kernel": "attn_fwd_bf16_kernel<128,false> over all chunks (event-timed per "
-                               "cpattn_fwd_chunks call, plan upload included)",
+                               "cpattn_fwd_chunks call)",
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
                      "flops_per_launch": attn_flops_per_launch},
         "schedules": schedules,

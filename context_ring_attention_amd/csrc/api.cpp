@@ -13,21 +13,21 @@ void clear_error();
 
 namespace {
 
-// Plans are built on the host and copied into the caller's device workspace
-// with an asynchronous copy on the caller's stream.  The copy's source must
-// stay valid until the copy has run, so plans are staged in a pinned host ring
-// that the library owns (one per device, created on first use and kept for the
-// life of the process).  Before a region of the ring is reused, the event
-// recorded after the copy that last read it is waited on; in steady state
-// those copies finished long ago and the wait returns at once.
+// Plans are built on the host into a pinned host ring that the library owns (one per device,
+// created on first use and kept for the life of the process), and the kernels read them from
+// there directly: a work-group reads its few plan records once, and no copy sits between
+// consecutive launches on the stream.  A region of the ring is reused only after the event
+// recorded behind the launches that read it has completed; in steady state those launches
+// finished long ago and the check returns at once.
 class StagingRing {
  public:
   static constexpr size_t kCapacity = size_t(8) << 20;
   static constexpr size_t kAlign = 256;
 
-  // Copy `bytes` produced by `fill` into device memory `dst` on `stream`.
-  template <class Fill>
-  cpattn_status upload(void* dst, size_t bytes, hipStream_t stream, Fill&& fill) {
+  // Write `bytes` with `fill` into a free region of the ring, then `launch(region)` enqueues on
+  // `stream` the kernels that read it; the region is held until they have run.
+  template <class Fill, class Launch>
+  cpattn_status run(size_t bytes, hipStream_t stream, Fill&& fill, Launch&& launch) {
     std::lock_guard<std::mutex> lock(mu_);
     if (!host_) {
       if (hipHostMalloc(&host_, kCapacity, hipHostMallocDefault) != hipSuccess) {
@@ -56,8 +56,8 @@ class StagingRing {
     }
     char* src = static_cast<char*>(host_) + begin;
     fill(src);
-    if (hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
-      return set_error(CPATTN_ERR_HIP, "hipMemcpyAsync of the plan failed");
+    const cpattn_status st = launch(static_cast<const char*>(src));
+    if (st != CPATTN_OK) return st;  // nothing was enqueued: the region stays free
     hipEvent_t ev;
     if (!spare_.empty()) {
       ev = spare_.back();
@@ -237,12 +237,12 @@ cpattn_status fwd_impl(const void* q, const void* const* ks, const void* const* 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
     return set_error(CPATTN_ERR_HIP, "hipGetDevice failed");
-  st = g_rings[dev].upload(workspace, plan_bytes, stream, [&](char* dst) {
+  auto fill = [&](char* dst) {
     build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal,
                   g, reinterpret_cast<cpattn_plan_entry*>(dst), n, nullptr);
-  });
-  if (st != CPATTN_OK) return st;
-  const auto* plan = static_cast<const cpattn_plan_entry*>(workspace);
+  };
+  auto launch = [&](const char* staged) -> cpattn_status {
+  const auto* plan = reinterpret_cast<const cpattn_plan_entry*>(staged);
   hipError_t err;
   if (dtype == CPATTN_BF16) {
     ChunkPtrs<__bf16> kv{};
@@ -264,6 +264,8 @@ cpattn_status fwd_impl(const void* q, const void* const* ks, const void* const* 
   if (err != hipSuccess)
     return set_error(CPATTN_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
   return CPATTN_OK;
+  };
+  return g_rings[dev].run(plan_bytes, stream, fill, launch);
 }
 
 }  // namespace
@@ -304,9 +306,12 @@ cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void
 namespace {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// The two plans are staged in the pinned ring (query plan, then key plan at key_plan_at);
+// the device workspace holds delta and the log2-scaled LSE.
 struct BwdLayout {
   int64_t n_q, n_k;        // tiles of the query plan and of the key plan
-  size_t key_plan_at, delta_at, lse2_at, plan_bytes, total;
+  size_t key_plan_at, plan_bytes;  // in the staging ring
+  size_t delta_at, lse2_at, total; // in the workspace
 };
 
 BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq) {
@@ -315,7 +320,7 @@ BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq) {
   l.n_k = n_k;
   l.key_plan_at = align256(size_t(n_q) * sizeof(cpattn_plan_entry));
   l.plan_bytes = l.key_plan_at + size_t(n_k) * sizeof(cpattn_plan_entry);
-  l.delta_at = align256(l.plan_bytes);
+  l.delta_at = 0;
   l.lse2_at = align256(l.delta_at + size_t(tq) * hq * sizeof(float));
   l.total = std::max<size_t>(256, l.lse2_at + size_t(tq) * hq * sizeof(float));
   return l;
@@ -415,15 +420,12 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
     return set_error(CPATTN_ERR_HIP, "hipGetDevice failed");
-  st = g_rings[dev].upload(workspace, lay.plan_bytes, stream, [&](char* dst) {
+  auto fill = [&](char* dst) {
     build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal, g,
                   reinterpret_cast<cpattn_plan_entry*>(dst), n_qt, nullptr);
     build_key_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq,
                       causal, reinterpret_cast<KeyTile*>(dst + lay.key_plan_at), lay.n_k);
-  });
-  if (st != CPATTN_OK) return st;
-  const auto* qplan = reinterpret_cast<const cpattn_plan_entry*>(ws);
-  const auto* kplan = reinterpret_cast<const KeyTile*>(ws + lay.key_plan_at);
+  };
   float* delta = reinterpret_cast<float*>(ws + lay.delta_at);
   float* lse2 = reinterpret_cast<float*>(ws + lay.lse2_at);
   ChunkPtrs<__bf16> kv{};
@@ -434,16 +436,21 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
     dkv.k[c] = dks[c];
     dkv.v[c] = dvs[c];
   }
-  hipError_t err = launch_bwd_delta(do_, o, lse, int(tq), hq, d, delta, lse2, stream);
-  if (err == hipSuccess)
-    err = launch_bwd_dq(q, kv, nchunks, do_, lse, delta, qplan, int(n_qt), head_groups,
-                        g.heads_per_tile, hq, hkv, d, int(tq), dq, stream);
-  if (err == hipSuccess)
-    err = launch_bwd_dkdv(q, kv, do_, lse2, delta, kplan, int(lay.n_k), hq, hkv, d, int(tq), dkv,
-                          stream);
-  if (err != hipSuccess)
-    return set_error(CPATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
-  return CPATTN_OK;
+  auto launch = [&](const char* staged) -> cpattn_status {
+    const auto* qplan = reinterpret_cast<const cpattn_plan_entry*>(staged);
+    const auto* kplan = reinterpret_cast<const KeyTile*>(staged + lay.key_plan_at);
+    hipError_t err = launch_bwd_delta(do_, o, lse, int(tq), hq, d, delta, lse2, stream);
+    if (err == hipSuccess)
+      err = launch_bwd_dq(q, kv, nchunks, do_, lse, delta, qplan, int(n_qt), head_groups,
+                          g.heads_per_tile, hq, hkv, d, int(tq), dq, stream);
+    if (err == hipSuccess)
+      err = launch_bwd_dkdv(q, kv, do_, lse2, delta, kplan, int(lay.n_k), hq, hkv, d, int(tq), dkv,
+                            stream);
+    if (err != hipSuccess)
+      return set_error(CPATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
+    return CPATTN_OK;
+  };
+  return g_rings[dev].run(lay.plan_bytes, stream, fill, launch);
 }
 
 cpattn_status cpattn_bwd_chunk(const void* q, const void* k, const void* v, const float* o,

@@ -58,11 +58,17 @@ typedef enum {
 } cpattn_dtype;
 
 /*
- * Bytes of device workspace one cpattn_fwd_chunk call needs for these query
- * sequences (the work plan).  cu_seqlens_q is host int32 [nseq + 1].  The value
- * depends only on nseq, the query lengths and the head counts, so one workspace
- * serves every KV chunk of a rank's share.  Returns 0 if the arguments are
- * invalid (nseq < 0, null cu_seqlens_q with nseq > 0, hq or hkv < 1).
+ * Bytes of device workspace one cpattn_fwd_chunk call takes for these query
+ * sequences (room for the work plan).  cu_seqlens_q is host int32 [nseq + 1].  The
+ * value depends only on nseq, the query lengths and the head counts, so one
+ * workspace serves every KV chunk of a rank's share.  Returns 0 if the arguments
+ * are invalid (nseq < 0, null cu_seqlens_q with nseq > 0, hq or hkv < 1).
+ *
+ * Work plans: every call builds its plan on the host into a pinned host ring that
+ * the library allocates once per device (8 MiB, kept for the life of the process)
+ * and the kernels read it from there; a region of the ring is reused only after
+ * the launches that read it have completed.  The forward entry points validate
+ * the workspace but do not write it (it is reserved for the library).
  */
 size_t cpattn_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q, int32_t hq, int32_t hkv,
                              int32_t d);
@@ -93,8 +99,8 @@ size_t cpattn_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_q, i
  *   q_pos_offset, k_pos_offset   host int32 [nseq], >= 0, or NULL for all zeros
  *   hq % hkv == 0; d in {64, 128}
  *   workspace        device, >= cpattn_workspace_size(...) bytes, 256-byte aligned;
- *                    owned by the caller; it holds this call's work plan until the
- *                    kernel has run, so consecutive calls on one stream may reuse it.
+ *                    owned by the caller, reserved for the library (see above);
+ *                    consecutive calls on one stream may reuse it.
  * The caller owns every buffer; o must not overlap q, k or v.  Rows of o/lse for
  * queries of zero-length key sequences are written as (0, -inf).
  * Returns CPATTN_OK, or an error code with nothing enqueued.
@@ -174,7 +180,8 @@ cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void
  *   dq        device [Tq, hq, d] fp32; dk, dv device [Tk, hkv, d] fp32   (read and written)
  *   metadata  as cpattn_fwd_chunk (host); dtype must be CPATTN_BF16; d in {64, 128}
  *   workspace device, >= cpattn_bwd_workspace_size(...) bytes, 256-byte aligned; it holds
- *             the plans, delta and the log2-scaled LSE until the kernels have run
+ *             delta and the log2-scaled LSE until the kernels have run (the plans are
+ *             staged in the library's pinned ring, see cpattn_workspace_size)
  * Rows whose LSE is -inf (no visible key in the share) contribute nothing.  No output may
  * overlap an input or another output.  Returns CPATTN_OK, or an error code with nothing
  * enqueued (CPATTN_ERR_UNSUPPORTED for fp32 inputs).
@@ -209,8 +216,8 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Bytes of device workspace one cpattn_bwd_chunk call needs (plans of both kernels,
- * delta [hq, Tq] and the LSE in log2 units [hq, Tq], fp32).  Returns 0 for invalid arguments.
+ * Bytes of device workspace one cpattn_bwd_chunk call needs (delta [hq, Tq] and the
+ * LSE in log2 units [hq, Tq], fp32).  Returns 0 for invalid arguments.
  */
 size_t cpattn_bwd_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_k, int32_t hq, int32_t hkv, int32_t d);
