@@ -30,7 +30,9 @@ class StagingRing {
   cpattn_status run(size_t bytes, hipStream_t stream, Fill&& fill, Launch&& launch) {
     std::lock_guard<std::mutex> lock(mu_);
     if (!host_) {
-      if (hipHostMalloc(&host_, kCapacity, hipHostMallocDefault) != hipSuccess) {
+      // Coherent (fine-grained) host memory: the GPU never serves a kernel's read of a reused
+      // region from a cache line filled by an earlier launch.
+      if (hipHostMalloc(&host_, kCapacity, hipHostMallocCoherent) != hipSuccess) {
         host_ = nullptr;
         return set_error(CPATTN_ERR_HIP, "hipHostMalloc of the plan staging ring failed");
       }

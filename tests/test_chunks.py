@@ -199,6 +199,35 @@ def test_cp4_share_stream_full_size_every_row_of_one_head(gpu_lib):
         check(o_h[:, head:head + 1], l_h[head:head + 1], o_ref, l_ref, "bf16", f"cp4 head {head}")
 
 
+def test_plan_ring_reuse_is_exact(gpu_lib):
+    """Plans are staged in a fixed pinned ring that the kernels read in place; after the ring
+    has wrapped around several times (two different packs alternating, ~64 KB of plan each,
+    300 calls), every result is still bitwise the first one of its pack."""
+    import torch
+    rng = np.random.default_rng(31)
+    packs = []
+    for _ in range(2):
+        q, k, v, cu_q, cu_k, qo, ko = wl.random_pack(rng, 5, 1200, 32, 8, 128, dtype="bf16", min_len=400)
+        rows, cus, offs = _split(rng, k, v, cu_k, ko, 16)
+        Q = dev(q, "bfloat16")
+        ks = [dev(k[r], "bfloat16") for r in rows]
+        vs = [dev(v[r], "bfloat16") for r in rows]
+        o, lse = gpu_lib.cpattn_fwd_chunks(Q, ks, vs, cu_q, cus, qo, offs)
+        torch.cuda.synchronize()
+        ent, _ = gpu_lib.cpattn_plan_build_chunks(cu_q, cus, qo, offs, hq=32, hkv=8, d=128)
+        packs.append((Q, ks, vs, cu_q, cus, qo, offs, o.clone(), lse.clone(), ent.nbytes))
+    staged = sum(p[-1] for p in packs) * 150
+    assert staged > 2 * (8 << 20), "the calls must wrap the 8 MiB ring"
+    outs = [(torch.empty_like(p[7]), torch.empty_like(p[8])) for p in packs]
+    for it in range(150):
+        for (Q, ks, vs, cu_q, cus, qo, offs, o_ref, l_ref, _), (o, lse) in zip(packs, outs):
+            gpu_lib.cpattn_fwd_chunks(Q, ks, vs, cu_q, cus, qo, offs, out=o, lse=lse)
+        if it % 10 == 9:
+            torch.cuda.synchronize()
+            for p, (o, lse) in zip(packs, outs):
+                assert torch.equal(o, p[7]) and torch.equal(lse, p[8]), f"call pair {it}"
+
+
 def test_too_many_chunks_is_rejected(gpu_lib):
     import torch
     q = dev(np.ones((4, 2, 64), np.float32), "bfloat16")
