@@ -244,28 +244,28 @@ cpattn_status fwd_impl(const void* q, const void* const* ks, const void* const* 
                   g, reinterpret_cast<cpattn_plan_entry*>(dst), n, nullptr);
   };
   auto launch = [&](const char* staged) -> cpattn_status {
-  const auto* plan = reinterpret_cast<const cpattn_plan_entry*>(staged);
-  hipError_t err;
-  if (dtype == CPATTN_BF16) {
-    ChunkPtrs<__bf16> kv{};
-    for (int32_t c = 0; c < nchunks; ++c) {
-      kv.k[c] = static_cast<const __bf16*>(ks[c]);
-      kv.v[c] = static_cast<const __bf16*>(vs[c]);
+    const auto* plan = reinterpret_cast<const cpattn_plan_entry*>(staged);
+    hipError_t err;
+    if (dtype == CPATTN_BF16) {
+      ChunkPtrs<__bf16> kv{};
+      for (int32_t c = 0; c < nchunks; ++c) {
+        kv.k[c] = static_cast<const __bf16*>(ks[c]);
+        kv.v[c] = static_cast<const __bf16*>(vs[c]);
+      }
+      err = launch_attn_fwd_bf16(q, kv, nchunks, plan, int(n), head_groups, g.heads_per_tile, hq,
+                                 hkv, d, int(tq), accumulate != 0, o, lse, stream);
+    } else {
+      ChunkPtrs<float> kv{};
+      for (int32_t c = 0; c < nchunks; ++c) {
+        kv.k[c] = static_cast<const float*>(ks[c]);
+        kv.v[c] = static_cast<const float*>(vs[c]);
+      }
+      err = launch_attn_fwd_f32(static_cast<const float*>(q), kv, nchunks, plan, int(n), hq, hkv, d,
+                                int(tq), accumulate != 0, o, lse, stream);
     }
-    err = launch_attn_fwd_bf16(q, kv, nchunks, plan, int(n), head_groups, g.heads_per_tile, hq,
-                               hkv, d, int(tq), accumulate != 0, o, lse, stream);
-  } else {
-    ChunkPtrs<float> kv{};
-    for (int32_t c = 0; c < nchunks; ++c) {
-      kv.k[c] = static_cast<const float*>(ks[c]);
-      kv.v[c] = static_cast<const float*>(vs[c]);
-    }
-    err = launch_attn_fwd_f32(static_cast<const float*>(q), kv, nchunks, plan, int(n), hq, hkv, d,
-                              int(tq), accumulate != 0, o, lse, stream);
-  }
-  if (err != hipSuccess)
-    return set_error(CPATTN_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
-  return CPATTN_OK;
+    if (err != hipSuccess)
+      return set_error(CPATTN_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
+    return CPATTN_OK;
   };
   return g_rings[dev].run(plan_bytes, stream, fill, launch);
 }
