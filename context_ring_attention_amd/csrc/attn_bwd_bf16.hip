@@ -99,21 +99,30 @@ __device__ __forceinline__ void load_tile(const __bf16* base, int64_t first, int
   }
 }
 
-// S-like product: C[32 rows of a][32 cols] over d, A rows read from an LDS tile (row r0 + lane%32),
-// B fragments in registers.  Two tiles (rows 0-31 and 32-63) accumulate into c0, c1.
-template <int D, bool BOTH>
-__device__ __forceinline__ void rows_product(const char* tile, const bf16x8* bf, int n, int g,
-                                             f32x16& c0, f32x16& c1) {
+// Two S-like products at once: C[32 rows][32 cols] over d for rows 0-31 and 32-63 of an LDS
+// tile (row n of the lane's tile, lane % 32) against B fragments in registers, for tile_a x
+// bf_a into c0, c1 and tile_b x bf_b into e0, e1; the k-steps are interleaved so that four
+// independent accumulation chains keep the matrix core busy.
+template <int D, bool BOTH_A, bool BOTH_B>
+__device__ __forceinline__ void rows_product2(const char* tile_a, const bf16x8* bf_a,
+                                              const char* tile_b, const bf16x8* bf_b, int n, int g,
+                                              f32x16& c0, f32x16& c1, f32x16& e0, f32x16& e1) {
   using T = Tile<D>;
   constexpr int KS = D / 16;
   c0 = f32x16{};
   c1 = f32x16{};
+  e0 = f32x16{};
+  e1 = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(tile + T::template off<BOTH>(n, 2 * ks + g));
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(tile + T::template off<BOTH>(32 + n, 2 * ks + g));
-    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bf[ks], c0, 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bf[ks], c1, 0, 0, 0);
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(tile_a + T::template off<BOTH_A>(n, 2 * ks + g));
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(tile_a + T::template off<BOTH_A>(32 + n, 2 * ks + g));
+    const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(tile_b + T::template off<BOTH_B>(n, 2 * ks + g));
+    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(tile_b + T::template off<BOTH_B>(32 + n, 2 * ks + g));
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bf_a[ks], c0, 0, 0, 0);
+    e0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, bf_b[ks], e0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bf_a[ks], c1, 0, 0, 0);
+    e1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, bf_b[ks], e1, 0, 0, 0);
   }
 }
 
@@ -285,8 +294,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         const char* kt = smem + stage * kStage;
         const char* vt = kt + T::kBytes;
         f32x16 s0, s1, p0, p1;
-        rows_product<D, true>(kt, qf, n, g, s0, s1);        // S^T = K Q^T
-        rows_product<D, false>(vt, dof, n, g, p0, p1);      // dP^T = V dO^T
+        // S^T = K Q^T and dP^T = V dO^T
+        rows_product2<D, true, false>(kt, qf, vt, dof, n, g, s0, s1, p0, p1);
         const int lim = (decltype(masked)::value && j >= nfull_w)
                             ? min(pe.k_len - 1, pe.delta + tok0 + n) - j * BN - 4 * g
                             : BN;
@@ -423,8 +432,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int tb = t_first + j * QB + 4 * g;
     const int lo = pe.delta + key, hi_excl = pe.q_len;
     f32x16 s0, s1, p0, p1;
-    rows_product<D, true>(qt, kf, n, g, s0, s1);   // S = Q K^T   (rows: tokens)
-    rows_product<D, true>(dt_, vf, n, g, p0, p1);  // dP = dO V^T
+    // S = Q K^T and dP = dO V^T (rows: tokens)
+    rows_product2<D, true, true>(qt, kf, dt_, vf, n, g, s0, s1, p0, p1);
     bf16x8 pb[4], db[4];
     f32x16 ps0, ps1;
     // Registers 4 i .. 4 i + 3 of tile tt hold rows 32 tt + 8 i + 4 g .. + 3: their lse2 and
