@@ -35,8 +35,8 @@ ATTN_SOURCE = os.path.join(HERE, "context_ring_attention_amd", "csrc", "attn_fwd
 # (scaled by a plain-copy calibration), keyed by workload and the sha256 of the kernel source
 # they were taken on.  Any other pair reports traffic as null until it is profiled again.
 PROFILED_TRAFFIC = {
-    ("cp4_share", "d10ef45935ad77971220ad11ea0fddab51b8812736092d9dafd710da2197323a"): 223390240,
-    ("ctx128k_share", "d10ef45935ad77971220ad11ea0fddab51b8812736092d9dafd710da2197323a"): 3136331797,
+    ("cp4_share", "d10ef45935ad77971220ad11ea0fddab51b8812736092d9dafd710da2197323a"): 223394549,
+    ("ctx128k_share", "d10ef45935ad77971220ad11ea0fddab51b8812736092d9dafd710da2197323a"): 2939329515,
 }
 
 
