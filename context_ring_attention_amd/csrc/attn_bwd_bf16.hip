@@ -415,7 +415,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // and the ragged end): j in [j_full0, j_full1) of every head; the steps of a head run in
   // three loops (masked, unmasked, masked) so each loop body is one straight copy of the step.
   const bool tile_full = pe.nrows == kBwdKeysPerTile;
-  const int j_full0 = tile_full ? min(nblk, max(0, (pe.delta + kBwdKeysPerTile - 1 - t_first + QB - 1) / QB)) : nblk;
+  // first block whose first query sees the tile's last key, and blocks wholly inside the sequence
+  const int lead = pe.delta + kBwdKeysPerTile - 1 - t_first;
+  const int j_full0 = tile_full ? min(nblk, max(0, (lead + QB - 1) / QB)) : nblk;
   const int j_full1 = tile_full ? max(j_full0, min(nblk, (pe.q_len - t_first) / QB)) : nblk;
   auto run_step = [&](int step, auto masked) {
     const int stage = step & 1;
