@@ -164,6 +164,67 @@ def test_backward_cp4_share_full_size_one_group(gpu_lib):
         check_grad(host(dvs[c])[:, 0:1], rv[rows], f"cp4 dv chunk {c}")
 
 
+def test_backward_ctx128k_share_full_size(gpu_lib):
+    """The 128K share (one sequence, 32768 queries at offset 98304, 4 key chunks of 32768,
+    8 query heads on one kv head) at full size, in the benchmark's launch configuration.
+
+    The oracle cannot differentiate the whole share in seconds, so it checks what it can
+    compute exactly, and identities of the gradient cover the rest:
+      * the last 160 queries are the only ones that see the last 160 keys: the oracle's
+        backward over those queries (each against all its keys) gives their dq and those
+        keys' dk, dv exactly (one full key tile and part of the one before);
+      * dq of a few more rows, each from the oracle's backward over that row alone;
+      * each row's softmax sums to one, so the dv of all keys sums to the dO of all rows
+        and query heads; the dS of a row sums to zero (delta is rowsum(P * dP)), so the dk
+        of all keys sums to zero.
+    Tolerance of the identities: rounding P and dS to bf16 leaves each row's sums off by
+    about 2^-9 of a row's single terms, which over 2^18 (row, head) pairs adds up to about
+    1e-5 of |sum dO| for dv and about 3e-3 of |dk| for dk; the bars are 1e-3 and 3e-2
+    (leaving delta out of dS gives a dk sum larger than |dk|).
+    """
+    import torch
+    w = wl.make("ctx128k_share", 0)
+    g = w.groups[0]
+    assert len(g.cu_q) == 2 and g.k_full.shape[1] == 1
+    rng = np.random.default_rng(128)
+    do = wl.round_to_bf16(rng.standard_normal(g.q.shape, dtype=np.float32))
+    Q, DO = dev(g.q, "bfloat16"), dev(do, "bfloat16")
+    ks = [dev(c.k, "bfloat16") for c in g.chunks]
+    vs = [dev(c.v, "bfloat16") for c in g.chunks]
+    cus = [c.cu_k for c in g.chunks]
+    offs = [c.k_off for c in g.chunks]
+    o, lse = gpu_lib.cpattn_fwd_chunks(Q, ks, vs, g.cu_q, cus, g.q_off, offs)
+    dq, dks, dvs = gpu_lib.cpattn_share_bwd(Q, ks, vs, o, lse, DO, g.cu_q, cus, g.q_off, offs)
+    torch.cuda.synchronize()
+    dq = host(dq)
+    dk = np.zeros(g.k_full.shape); dv = np.zeros(g.v_full.shape)
+    for c, ch in enumerate(g.chunks):
+        a = int(ch.k_off[0])
+        dk[a:a + ch.k.shape[0]] = host(dks[c]); dv[a:a + ch.k.shape[0]] = host(dvs[c])
+    tq, nk, q0 = g.q.shape[0], g.k_full.shape[0], int(g.q_off[0])
+    assert q0 + tq == nk
+    # the last m queries and the last m keys
+    m = 160
+    kk = np.array([0, nk], np.int64)
+    rq, rk, rv = attention_bwd_ref(g.q[tq - m:], g.k_full, g.v_full, do[tq - m:], [0, m], kk,
+                                   [q0 + tq - m], [0], True)
+    check_grad(dq[tq - m:], rq, "128k dq, last rows")
+    check_grad(dk[nk - m:], rk[nk - m:], "128k dk, last keys")
+    check_grad(dv[nk - m:], rv[nk - m:], "128k dv, last keys")
+    for t in [0, 1, 127, 128, 16383, int(rng.integers(0, tq - m))]:
+        rq1, _, _ = attention_bwd_ref(g.q[t:t + 1], g.k_full, g.v_full, do[t:t + 1], [0, 1], kk,
+                                      [q0 + t], [0], True)
+        check_grad(dq[t:t + 1], rq1, f"128k dq row {t}")
+    # identities over all keys
+    sum_do = do.astype(np.float64).sum(axis=(0, 1))
+    sum_dv = dv.sum(axis=(0, 1))
+    rel_v = float(np.linalg.norm(sum_dv - sum_do) / np.linalg.norm(sum_do))
+    rel_k = float(np.linalg.norm(dk.sum(axis=(0, 1))) / np.linalg.norm(dk))
+    print(f"128k identities: |sum dv - sum dO| / |sum dO| {rel_v:.2e}, |sum dk| / |dk| {rel_k:.2e}")
+    assert rel_v <= 1e-3, f"dv does not sum to the rows' dO: {rel_v:.3e}"
+    assert rel_k <= 3e-2, f"dk does not sum to zero: {rel_k:.3e}"
+
+
 def test_backward_rejects_fp32(gpu_lib):
     import torch
     q = torch.zeros((4, 2, 64), device="cuda")
