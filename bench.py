@@ -8,7 +8,9 @@ walks every KV chunk of the share with the online softmax carried across chunks
 causal FLOPs (4 * D * Hq per visible query/key pair) divided by the step time.
 The two other schedules of the same share -- per-chunk launches accumulating in
 the epilogue (cpattn_fwd_chunk_accum), and per-chunk partials merged by
-cpattn_merge -- are timed the same way and reported under "schedules".
+cpattn_merge -- are timed the same way and reported under "schedules".  Further seeds of the
+CP4 share (other packs of the same shapes) are timed like the step and reported under "seeds",
+with the aggregate over all of them (total FLOPs / total time).
 Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload cp4_share] [--seed 0]
@@ -97,6 +99,9 @@ def main() -> int:
                          "always timed, last)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward of the share (reported under 'backward')")
+    ap.add_argument("--sweep-seeds", default=None,
+                    help="comma-separated further seeds of the workload whose step is timed the same "
+                         "way (reported under 'seeds'; default 1,2,3,4 for cp4_share, none otherwise)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain elementwise copy of MIB MiB "
                          "(reference point for HBM byte counters)")
@@ -257,6 +262,62 @@ def main() -> int:
                     "counted_as": "10 D Hq per visible pair (5 products of the forward's 2 D Hq)",
                     "launches_per_step": "delta, dQ over all chunks, dK/dV over all chunks"}
 
+    # Other packs of the same workload (further seeds: same shapes, other sequence lengths), the
+    # step timed the same way, and the aggregate over all of them (total FLOPs / total time).
+    sweep = args.sweep_seeds if args.sweep_seeds is not None else (
+        "1,2,3,4" if args.workload == "cp4_share" else "")
+    seeds = None
+    sweep_list = [int(x) for x in sweep.split(",") if x.strip() and int(x) != w.seed]
+    if sweep_list:
+        per_seed = [{"seed": w.seed, "pieces": [int(x) for x in np.diff(cu_q)],
+                     "ms_per_step": round(ms_step, 4), "tflops": round(value, 2)}]
+        tot_flops, tot_ms = flops_step, ms_step
+        for sd in sweep_list:
+            w2 = wl.make(args.workload, sd)
+            g2 = w2.groups[0]
+            q2 = torch.from_numpy(g2.q).to("cuda", bf)
+            ks2 = [torch.from_numpy(c.k).to("cuda", bf) for c in g2.chunks]
+            vs2 = [torch.from_numpy(c.v).to("cuda", bf) for c in g2.chunks]
+            cu_q2 = np.ascontiguousarray(g2.cu_q, np.int32)
+            q_off2 = np.ascontiguousarray(g2.q_off, np.int32)
+            cu_ks2 = [np.ascontiguousarray(c.cu_k, np.int32) for c in g2.chunks]
+            k_offs2 = [np.ascontiguousarray(c.k_off, np.int32) for c in g2.chunks]
+            bufs2 = cra.ShareBuffers.allocate(q2, w2.hkv, cu_q2, len(g2.chunks))
+            flops2 = sum(4 * w2.d * w2.hq * visible_pairs(cu_q2, c.cu_k, q_off2, c.k_off)
+                         for c in g2.chunks)
+
+            def step2():
+                cra.cpattn_fwd_chunks(q2, ks2, vs2, cu_q2, cu_ks2, q_off2, k_offs2, True,
+                                      out=bufs2.o_acc, lse=bufs2.lse_acc, workspace=bufs2.workspace,
+                                      stream=stream)
+
+            for _ in range(args.warmup):
+                step2()
+            torch.cuda.synchronize()
+            gc.collect()
+            gc.freeze()
+            gc.disable()
+            try:
+                s0, s1 = ev(), ev()
+                s0.record(stream)
+                for _ in range(args.steps):
+                    step2()
+                s1.record(stream)
+                torch.cuda.synchronize()
+            finally:
+                gc.enable()
+                gc.unfreeze()
+            ms2 = s0.elapsed_time(s1) / args.steps
+            per_seed.append({"seed": sd, "pieces": [int(x) for x in np.diff(cu_q2)],
+                             "ms_per_step": round(ms2, 4),
+                             "tflops": round(flops2 / (ms2 / 1e3) / 1e12, 2)})
+            tot_flops += flops2
+            tot_ms += ms2
+            del q2, ks2, vs2, bufs2
+        seeds = {"per_seed": per_seed,
+                 "aggregate_tflops": round(tot_flops / (tot_ms / 1e3) / 1e12, 2),
+                 "aggregate_frac": round(tot_flops / (tot_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
     import hashlib
     with open(ATTN_SOURCE, "rb") as f:
         traffic = PROFILED_TRAFFIC.get((args.workload, hashlib.sha256(f.read()).hexdigest()))
@@ -292,6 +353,7 @@ def main() -> int:
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
                      "flops_per_launch": attn_flops_per_launch},
         "schedules": schedules,
+        "seeds": seeds,
         "backward": backward,
         "merge": {"schedule": "merge", "avg_launch_us": round(merge_avg_ms * 1e3, 2) if timed_merge else None,
                   "bytes_per_launch": merge_bytes, "achieved_GBs": round(merge_gbs, 1) if merge_gbs else None,
