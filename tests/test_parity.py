@@ -74,6 +74,17 @@ def test_cp4_share_full_size(gpu_lib):
         check(host(oc)[rows], host(lc)[:, rows], *ref, "bf16", f"cp4 chunk {c}")
 
 
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_cp4_share_other_packs(gpu_lib, seed):
+    """The other packs the benchmark times (same shapes, other sequence lengths), through the
+    benchmarked call: one launch over all chunks."""
+    w = wl.make("cp4_share", seed)
+    g = w.groups[0]
+    rows = sample_rows(g.cu_q, 32, extra=128, seed=seed)
+    _, _, _, o, lse = _run_group(gpu_lib, w, g, rows, "stream")
+    check(o, lse, *share_ref(g, rows=rows), "bf16", f"cp4 share seed {seed}")
+
+
 def test_ctx128k_share_full_size(gpu_lib):
     w = wl.make("ctx128k_share", 0)
     g = w.groups[0]
