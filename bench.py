@@ -215,6 +215,23 @@ def main() -> int:
     merge_ms = sum(a.elapsed_time(b) for row in merge_ev for a, b in row) if timed_merge else 0.0
     merge_avg_ms = merge_ms / max(1, args.steps * n_merge)
     merge_gbs = merge_bytes / (merge_avg_ms / 1e3) / 1e9 if timed_merge else None
+    # Reference for the merge's HBM roof: torch's elementwise add over buffers of O's size (two
+    # reads and one write, the merge's traffic without the LSE rows), timed the same way.
+    add_gbs = None
+    if timed_merge:
+        xa, xb = bufs.o_acc, bufs.o_part
+        xc = torch.empty_like(xa)
+        for _ in range(3):
+            torch.add(xa, xb, out=xc)
+        torch.cuda.synchronize()
+        a0, a1 = ev(), ev()
+        a0.record(stream)
+        for _ in range(20):
+            torch.add(xa, xb, out=xc)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        add_gbs = 3 * xa.numel() * 4 / (a0.elapsed_time(a1) / 20 / 1e3) / 1e9
+        del xc
 
     backward = None
     if not args.no_backward:
@@ -357,7 +374,8 @@ def main() -> int:
         "backward": backward,
         "merge": {"schedule": "merge", "avg_launch_us": round(merge_avg_ms * 1e3, 2) if timed_merge else None,
                   "bytes_per_launch": merge_bytes, "achieved_GBs": round(merge_gbs, 1) if merge_gbs else None,
-                  "hbm_frac": round(merge_gbs / HBM_PEAK_GBS, 4) if merge_gbs else None},
+                  "hbm_frac": round(merge_gbs / HBM_PEAK_GBS, 4) if merge_gbs else None,
+                  "torch_add_same_bytes_GBs": round(add_gbs, 1) if add_gbs else None},
         "flops_per_step": flops_step,
         "cpu_baseline": None,
     }
