@@ -59,7 +59,7 @@ typedef enum {
 
 /*
  * Bytes of device workspace one cpattn_fwd_chunk call takes for these query
- * sequences (room for the work plan).  cu_seqlens_q is host int32 [nseq + 1].  The
+ * sequences (the size of the call's work plan, which is staged as described below).  cu_seqlens_q is host int32 [nseq + 1].  The
  * value depends only on nseq, the query lengths and the head counts, so one
  * workspace serves every KV chunk of a rank's share.  Returns 0 if the arguments
  * are invalid (nseq < 0, null cu_seqlens_q with nseq > 0, hq or hkv < 1).
@@ -78,7 +78,7 @@ size_t cpattn_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q, int32_t 
 
 /*
  * Bytes of device workspace one cpattn_fwd_chunks call with nchunks chunks needs
- * (the work plan holds one record per tile and chunk).  nchunks == 1 gives
+ * (the size of its work plan: one record per tile and chunk).  nchunks == 1 gives
  * cpattn_workspace_size().  Returns 0 for invalid arguments, including nchunks
  * outside 1 .. CPATTN_MAX_CHUNKS.
  */
