@@ -148,20 +148,24 @@ def test_backward_cp4_share_full_size_one_group(gpu_lib):
     cus = [c.cu_k for c in g.chunks]
     offs = [c.k_off for c in g.chunks]
     o, lse = gpu_lib.cpattn_fwd_chunks(Q, ks, vs, g.cu_q, cus, g.q_off, offs)
-    dq, dks, dvs = gpu_lib.cpattn_share_bwd(Q, ks, vs, o, lse, DO, g.cu_q, cus, g.q_off, offs)
-    torch.cuda.synchronize()
     sub = wl.Group(q=g.q[:, 0:4], cu_q=g.cu_q, q_off=g.q_off, chunks=[], k_full=g.k_full[:, 0:1],
                    v_full=g.v_full[:, 0:1], cu_full=g.cu_full)
     rq, rk, rv = share_bwd_ref(sub, do[:, 0:4])
-    check_grad(host(dq)[:, 0:4], rq, "cp4 dq")
-    # chunk c holds piece c of every sequence: map the oracle's full-sequence key rows
     lengths = np.diff(g.cu_full)
-    for c, ch in enumerate(g.chunks):
-        rows = np.concatenate([np.arange(g.cu_full[i] + int(ch.k_off[i]),
-                                         g.cu_full[i] + int(ch.k_off[i]) + int(ch.cu_k[i + 1] - ch.cu_k[i]))
-                               for i in range(len(lengths))])
-        check_grad(host(dks[c])[:, 0:1], rk[rows], f"cp4 dk chunk {c}")
-        check_grad(host(dvs[c])[:, 0:1], rv[rows], f"cp4 dv chunk {c}")
+    # one pass over all chunks, then the ring's order (one call per chunk, dq accumulating)
+    for per_chunk in (False, True):
+        dq, dks, dvs = gpu_lib.cpattn_share_bwd(Q, ks, vs, o, lse, DO, g.cu_q, cus, g.q_off, offs,
+                                                per_chunk=per_chunk)
+        torch.cuda.synchronize()
+        how = "per chunk" if per_chunk else "one pass"
+        check_grad(host(dq)[:, 0:4], rq, f"cp4 dq ({how})")
+        # chunk c holds piece c of every sequence: map the oracle's full-sequence key rows
+        for c, ch in enumerate(g.chunks):
+            rows = np.concatenate([np.arange(g.cu_full[i] + int(ch.k_off[i]),
+                                             g.cu_full[i] + int(ch.k_off[i]) + int(ch.cu_k[i + 1] - ch.cu_k[i]))
+                                   for i in range(len(lengths))])
+            check_grad(host(dks[c])[:, 0:1], rk[rows], f"cp4 dk chunk {c} ({how})")
+            check_grad(host(dvs[c])[:, 0:1], rv[rows], f"cp4 dv chunk {c} ({how})")
 
 
 def test_backward_ctx128k_share_full_size(gpu_lib):
