@@ -2,15 +2,26 @@
 """Benchmark: one CP4 rank's share of a 16,384-token packed budget on one MI355X.
 
 A step is one pass of the whole per-rank hot path on the share's inputs (already
-resident in HBM): host planning (into pinned memory the kernel reads) and ONE cpattn_fwd_chunks launch that
-walks every KV chunk of the share with the online softmax carried across chunks
-(the ring loop's merges done in registers).  `value` is the share's algorithmic
-causal FLOPs (4 * D * Hq per visible query/key pair) divided by the step time.
-The two other schedules of the same share -- per-chunk launches accumulating in
-the epilogue (cpattn_fwd_chunk_accum), and per-chunk partials merged by
-cpattn_merge -- are timed the same way and reported under "schedules".  Further seeds of the
-CP4 share (other packs of the same shapes) are timed like the step and reported under "seeds",
-with the aggregate over all of them (total FLOPs / total time).
+resident in HBM): host planning, the plan's upload into the caller's workspace, and
+ONE cpattn_fwd_chunks launch that walks every KV chunk of the share with the online
+softmax carried across chunks (the ring loop's merges done in registers).  `value`
+is the share's algorithmic causal FLOPs (4 * D * Hq per visible query/key pair)
+divided by the step time.  The two other schedules of the same share -- per-chunk
+launches accumulating in the epilogue (cpattn_fwd_chunk_accum), and per-chunk
+partials merged by cpattn_merge -- are timed the same way under "schedules".
+Further seeds of the CP4 share (other packs of the same shapes) are timed like the
+step under "seeds", with the aggregate over all of them.
+
+The other workloads (the 128K-context CP=4 share, the 4,096-token pack without
+chunking and the Dynamic-CP mixed pack) are timed the same way in the same run and
+reported under "workloads": a step is one cpattn_fwd_chunks launch per group of
+the workload (the mixed pack has one group per CP size), with step time,
+TFLOP/s, fraction of the bf16 MFMA peak and processed tokens.
+
+The CPU baseline (the fp64 oracle on a bounded row sample of the CP4 share, in a
+process pool over (row block, kv head) tasks) runs first, before the GPU is
+initialised, so the forked workers never inherit a GPU context.
+
 Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload cp4_share] [--seed 0]
@@ -19,6 +30,7 @@ from __future__ import annotations
 
 import argparse
 import gc
+import hashlib
 import json
 import os
 import sys
@@ -36,10 +48,9 @@ ATTN_SOURCE = os.path.join(HERE, "context_ring_attention_amd", "csrc", "attn_fwd
 # HBM bytes per streaming attention launch, from rocprofv3 FETCH_SIZE and WRITE_SIZE runs
 # (scaled by a plain-copy calibration), keyed by workload and the sha256 of the kernel source
 # they were taken on.  Any other pair reports traffic as null until it is profiled again.
-PROFILED_TRAFFIC = {
-    ("cp4_share", "d10ef45935ad77971220ad11ea0fddab51b8812736092d9dafd710da2197323a"): 223394549,
-    ("ctx128k_share", "d10ef45935ad77971220ad11ea0fddab51b8812736092d9dafd710da2197323a"): 2939329515,
-}
+PROFILED_TRAFFIC = {}
+# A pool for the CPU baseline never exceeds one GPU's share of the host's cores.
+MAX_CPU_WORKERS = 16
 
 
 def visible_pairs(cu_q, cu_k, q_off, k_off) -> int:
@@ -61,29 +72,227 @@ def pack_words(lengths) -> str:
     return f"a {total:,}-token THD pack of {len(lengths)} sequences"
 
 
-def cpu_baseline(w, g, budget_rows: int = 4096):
-    """Time the fp64 oracle on (a bounded row sample of) the same share, on the host CPU."""
-    from oracle import share_ref
+def describe(w) -> str:
+    """Text of a workload: what it is, with its sizes."""
+    if w.name == "dcp_mixed":
+        cps = [len(g.chunks) for g in w.groups]
+        return (f"dcp_mixed (seed {w.seed}): {pack_words(w.lengths)}, lognormal lengths, "
+                f"{len(w.groups)} groups by CP size {cps}, each sample's KV in cp chunks, "
+                f"{w.hq}/{w.hkv} heads, D={w.d}, causal")
+    g = w.groups[0]
+    nch = len(g.chunks)
+    tq = int(g.cu_q[-1])
+    if nch == 1:
+        return (f"{w.name} (seed {w.seed}): {pack_words(w.lengths)}, no chunking, "
+                f"{w.hq}/{w.hkv} heads, D={w.d}, causal")
+    return (f"{w.name} (seed {w.seed}): last CP{nch} rank of {pack_words(w.lengths)}, local Q "
+            f"{tq} tokens in {len(g.cu_q) - 1} sequences, {nch} KV chunks of "
+            f"{int(g.chunks[0].cu_k[-1])} tokens, {w.hq}/{w.hkv} heads, D={w.d}, causal")
+
+
+# ---------------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample, in a process pool.
+
+_POOL_DATA = {}
+
+
+def _pool_init():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:   # pragma: no cover - threadpoolctl missing
-        threads = 1
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:   # pragma: no cover - threadpoolctl missing: BLAS keeps its default
+        pass
+
+
+def _pool_task(task):
+    """One (row block, kv head) task: the oracle's attention for those rows and the query
+    heads of that kv head (their GQA group), against every visible key of the share."""
+    from oracle import attention_ref
+    rows, kvh = task
+    g = _POOL_DATA["group"]
+    hq, hkv = _POOL_DATA["hq"], _POOL_DATA["hkv"]
+    grp = hq // hkv
+    heads = slice(kvh * grp, (kvh + 1) * grp)
+    nseq = len(g.cu_q) - 1
+    attention_ref(g.q[:, heads], g.k_full[:, kvh:kvh + 1], g.v_full[:, kvh:kvh + 1], g.cu_q,
+                  g.cu_full, g.q_off, np.zeros(nseq, np.int64), causal=True, rows=rows)
+    return len(rows)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, budget_rows: int = 4096, block_rows: int = 256):
+    """Time the fp64 oracle on a row sample of the share, over a fork-based process pool."""
+    import multiprocessing as mp
+    g = w.groups[0]
+    workers = max(1, min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS))
     rng = np.random.default_rng(1234)
-    rows = np.sort(rng.choice(int(g.cu_q[-1]), size=min(budget_rows, int(g.cu_q[-1])), replace=False))
+    tq = int(g.cu_q[-1])
+    rows = np.sort(rng.choice(tq, size=min(budget_rows, tq), replace=False))
     seq = np.searchsorted(g.cu_q, rows, side="right") - 1
     pairs = 0
     for r, i in zip(rows, seq):
         pos = int(g.q_off[i]) + int(r - g.cu_q[i])
         pairs += min(pos + 1, int(g.cu_full[i + 1] - g.cu_full[i]))
+    tasks = [(rows[b:b + block_rows], kvh) for b in range(0, len(rows), block_rows)
+             for kvh in range(w.hkv)]
+    _POOL_DATA.update(group=g, hq=w.hq, hkv=w.hkv)
+    ctx = mp.get_context("fork")
     t0 = time.perf_counter()
-    share_ref(g, rows=rows)
+    with ctx.Pool(workers, initializer=_pool_init) as pool:
+        done = sum(pool.map(_pool_task, tasks, chunksize=1))
     dt = time.perf_counter() - t0
+    assert done == len(rows) * w.hkv
     flops = 4 * w.d * w.hq * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(rows)} random query rows of the share x all {w.hq} heads against all "
-                      f"their visible keys (fp64 numpy, {dt:.1f} s, {flops / 1e9:.1f} GFLOP)",
-            "seconds": dt}
+    return {"value": float(f"{flops / dt / 1e12:.4g}"), "unit": "TFLOP/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{len(rows)} random query rows of the {w.name} share (seed {w.seed}) x all "
+                      f"{w.hq} heads against all their visible keys: fp64 numpy, {len(tasks)} "
+                      f"(row block, kv head) tasks on {workers} worker processes with one BLAS "
+                      f"thread each, {dt:.1f} s, {flops / 1e9:.1f} GFLOP",
+            "cpu_model": cpu_model()}
+
+
+# ---------------------------------------------------------------------------------------------
+# GPU timing helpers.
+
+def timed_steps(step, steps: int, warmup: int, stream, ev):
+    """Run `step` warmup times, then time exactly `steps` of them between two events on the
+    stream (with the garbage collector frozen: a full collection mid-step idles the GPU)."""
+    import torch
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    gc.collect()
+    gc.freeze()
+    gc.disable()
+    try:
+        t_start, t_end = ev(), ev()
+        t_start.record(stream)
+        for i in range(steps):
+            step(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
+        gc.unfreeze()
+    return t_start.elapsed_time(t_end) / steps
+
+
+class GpuGroup:
+    """Device copies and host metadata of one group (a Q pack and its KV chunks)."""
+
+    def __init__(self, w, g):
+        import torch
+        import context_ring_attention_amd as cra
+        bf = torch.bfloat16
+        self.q = torch.from_numpy(g.q).to("cuda", bf)
+        self.ks = [torch.from_numpy(c.k).to("cuda", bf) for c in g.chunks]
+        self.vs = [torch.from_numpy(c.v).to("cuda", bf) for c in g.chunks]
+        self.cu_q = np.ascontiguousarray(g.cu_q, np.int32)
+        self.q_off = np.ascontiguousarray(g.q_off, np.int32)
+        self.cu_ks = [np.ascontiguousarray(c.cu_k, np.int32) for c in g.chunks]
+        self.k_offs = [np.ascontiguousarray(c.k_off, np.int32) for c in g.chunks]
+        self.nch = len(g.chunks)
+        self.bufs = cra.ShareBuffers.allocate(self.q, w.hkv, self.cu_q, self.nch)
+        self.pairs_chunk = [visible_pairs(self.cu_q, c.cu_k, self.q_off, c.k_off) for c in g.chunks]
+        self.flops = sum(4 * w.d * w.hq * p for p in self.pairs_chunk)
+        self.tq = int(self.cu_q[-1])
+        self.tk = sum(int(c[-1]) for c in self.cu_ks)
+        self.alg_bytes = (self.tq * w.hq * w.d * 2 + 2 * self.tk * w.hkv * w.d * 2
+                          + self.tq * w.hq * w.d * 4 + self.tq * w.hq * 4)
+
+    def fwd(self, stream):
+        import context_ring_attention_amd as cra
+        cra.cpattn_fwd_chunks(self.q, self.ks, self.vs, self.cu_q, self.cu_ks, self.q_off,
+                              self.k_offs, True, out=self.bufs.o_acc, lse=self.bufs.lse_acc,
+                              workspace=self.bufs.workspace, stream=stream)
+
+
+def time_backward(w, gg, steps, warmup, stream, ev, seed):
+    """The share's backward in one pass (cpattn_bwd_chunks) from its forward output."""
+    import torch
+    import context_ring_attention_amd as cra
+    gg.fwd(stream)
+    gen = torch.Generator(device="cuda").manual_seed(seed + 1)
+    dout = torch.randn(gg.q.shape, device="cuda", generator=gen).to(torch.bfloat16)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dq = torch.zeros(gg.q.shape, **f32)
+    dks = [torch.zeros(k.shape, **f32) for k in gg.ks]
+    dvs = [torch.zeros(v.shape, **f32) for v in gg.vs]
+    bws = torch.empty(max(cra.cpattn_bwd_workspace_size_chunks(len(gg.cu_q) - 1, gg.cu_q, gg.cu_ks,
+                                                               w.hq, w.hkv, w.d), 256),
+                      dtype=torch.uint8, device="cuda")
+
+    def step(_):
+        cra.cpattn_bwd_chunks(gg.q, gg.ks, gg.vs, gg.bufs.o_acc, gg.bufs.lse_acc, dout, gg.cu_q,
+                              gg.cu_ks, gg.q_off, gg.k_offs, True, dq=dq, dks=dks, dvs=dvs,
+                              workspace=bws, stream=stream)
+
+    ms = timed_steps(step, steps, max(1, warmup), stream, ev)
+    flops = 10 * w.d * w.hq * sum(gg.pairs_chunk)
+    del dq, dks, dvs, bws, dout
+    return {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+            "frac": round(flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "flops_per_step": flops,
+            "counted_as": "10 D Hq per visible pair (5 products of the forward's 2 D Hq)",
+            "launches_per_step": "delta, dQ over all chunks, dK/dV over all chunks"}
+
+
+def stored_traffic(workload: str):
+    with open(ATTN_SOURCE, "rb") as f:
+        return PROFILED_TRAFFIC.get((workload, hashlib.sha256(f.read()).hexdigest()))
+
+
+def time_workload(name, seed, steps, warmup, stream, ev, backward: bool):
+    """A step = one cpattn_fwd_chunks launch per group; returns the workload's report."""
+    import workloads as wl
+    w = wl.make(name, seed)
+    gs = [GpuGroup(w, g) for g in w.groups]
+    launch_ev = [[(ev(), ev()) for _ in gs] for _ in range(steps)]
+
+    def step(i):
+        for j, gg in enumerate(gs):
+            if i is not False:
+                launch_ev[i][j][0].record(stream)
+            gg.fwd(stream)
+            if i is not False:
+                launch_ev[i][j][1].record(stream)
+
+    ms = timed_steps(step, steps, warmup, stream, ev)
+    flops = sum(gg.flops for gg in gs)
+    launch_ms = [sum(r[j][0].elapsed_time(r[j][1]) for r in launch_ev) / steps
+                 for j in range(len(gs))]
+    kern_ms = sum(launch_ms)
+    tq = sum(gg.tq for gg in gs)
+    tk = sum(gg.tk for gg in gs)
+    rep = {"config": describe(w),
+           "ms_per_step": round(ms, 4),
+           "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+           "frac": round(flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "attn_launches_per_step": len(gs),
+           "attn_avg_launch_us": [round(x * 1e3, 2) for x in launch_ms],
+           "roofline": {"bound": "mfma", "achieved": round(flops / (kern_ms / 1e3) / 1e12, 2),
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(flops / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                        "traffic": stored_traffic(name) if len(gs) == 1 else None,
+                        "algorithmic_bytes_per_step": sum(gg.alg_bytes for gg in gs)},
+           "flops_per_step": flops,
+           "tokens_per_step": {"query": tq, "key": tk},
+           "query_tokens_per_s": round(tq / (ms / 1e3), 1)}
+    if backward and len(gs) == 1:
+        rep["backward"] = time_backward(w, gs[0], steps, warmup, stream, ev, seed)
+    del gs
+    return rep
 
 
 def main() -> int:
@@ -98,10 +307,13 @@ def main() -> int:
                     help="comma-separated schedules to time besides the step itself (stream is "
                          "always timed, last)")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip timing the backward of the share (reported under 'backward')")
+                    help="skip timing the backward of the shares (reported under 'backward')")
     ap.add_argument("--sweep-seeds", default=None,
                     help="comma-separated further seeds of the workload whose step is timed the same "
                          "way (reported under 'seeds'; default 1,2,3,4 for cp4_share, none otherwise)")
+    ap.add_argument("--other-workloads", default="ctx128k_share,pack,dcp_mixed",
+                    help="comma-separated workloads timed after the main one, reported under "
+                         "'workloads' (empty for none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain elementwise copy of MIB MiB "
                          "(reference point for HBM byte counters)")
@@ -111,48 +323,44 @@ def main() -> int:
               "multi-GPU path; each rank's share is what one GPU computes.", file=sys.stderr)
         return 2
 
-    import torch
     import workloads as wl
+    w = wl.make(args.workload, args.seed)
+    if len(w.groups) != 1 or w.dtype != "bf16":
+        print("the main workload must be a single-group bf16 share (the others go under "
+              "--other-workloads)", file=sys.stderr)
+        return 2
+    g = w.groups[0]
+
+    # The CPU baseline first: its fork-based pool must start before anything touches the GPU.
+    cb = None
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w)
+
+    import torch
     import context_ring_attention_amd as cra
 
     cra.load()
     torch.cuda.set_device(0)
-    w = wl.make(args.workload, args.seed)
-    if len(w.groups) != 1 or w.dtype != "bf16":
-        print("bench.py times single-group bf16 share workloads", file=sys.stderr)
-        return 2
-    g = w.groups[0]
-    bf = torch.bfloat16
-    q = torch.from_numpy(g.q).to("cuda", bf)
-    ks = [torch.from_numpy(c.k).to("cuda", bf) for c in g.chunks]
-    vs = [torch.from_numpy(c.v).to("cuda", bf) for c in g.chunks]
-    cu_q = np.ascontiguousarray(g.cu_q, np.int32)
-    q_off = np.ascontiguousarray(g.q_off, np.int32)
-    cu_ks = [np.ascontiguousarray(c.cu_k, np.int32) for c in g.chunks]
-    k_offs = [np.ascontiguousarray(c.k_off, np.int32) for c in g.chunks]
-    nch = len(g.chunks)
-    bufs = cra.ShareBuffers.allocate(q, w.hkv, cu_q, nch)
     stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    pairs_chunk = [visible_pairs(cu_q, c.cu_k, q_off, c.k_off) for c in g.chunks]
-    flops_chunk = [4 * w.d * w.hq * p for p in pairs_chunk]
-    flops_step = sum(flops_chunk)
-    tq = int(cu_q[-1])
+    gg = GpuGroup(w, g)
+    q, ks, vs, bufs = gg.q, gg.ks, gg.vs, gg.bufs
+    cu_q, q_off, cu_ks, k_offs, nch = gg.cu_q, gg.q_off, gg.cu_ks, gg.k_offs, gg.nch
+    flops_step = gg.flops
+    tq = gg.tq
     merge_bytes = 3 * (tq * w.hq * w.d * 4 + tq * w.hq * 4)
     n_merge = nch - 1
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)
     attn_ev = {m: [[(ev(), ev()) for _ in g.chunks] for _ in range(args.steps)] for m in cra.MODES}
     merge_ev = [[(ev(), ev()) for _ in range(n_merge)] for _ in range(args.steps)]
-
     spare_attn = [(ev(), ev()) for _ in g.chunks]        # recorded during warm-up, unread
     spare_merge = [(ev(), ev()) for _ in range(n_merge)]
 
-    def step(mode, a_ev, m_ev):
+    def share_step(mode, a_ev, m_ev):
         if mode == "stream":
             a_ev[0][0].record(stream)
-            cra.cpattn_fwd_chunks(q, ks, vs, cu_q, cu_ks, q_off, k_offs, True, out=bufs.o_acc,
-                                  lse=bufs.lse_acc, workspace=bufs.workspace, stream=stream)
+            gg.fwd(stream)
             a_ev[0][1].record(stream)
             return
         for c in range(nch):
@@ -169,27 +377,6 @@ def main() -> int:
                 cra.cpattn_merge(bufs.o_acc, bufs.lse_acc, bufs.o_part, bufs.lse_part, stream=stream)
                 m_ev[c - 1][1].record(stream)
 
-    def timed(mode):
-        for _ in range(args.warmup):
-            step(mode, spare_attn, spare_merge)
-        torch.cuda.synchronize()
-        # A full collection of the interpreter's heap takes tens of ms and would leave the GPU
-        # idle mid-step: collect now, freeze what exists, and keep the collector off while timing.
-        gc.collect()
-        gc.freeze()
-        gc.disable()
-        try:
-            t_start, t_end = ev(), ev()
-            t_start.record(stream)
-            for i in range(args.steps):
-                step(mode, attn_ev[mode][i], merge_ev[i])
-            t_end.record(stream)
-            torch.cuda.synchronize()
-        finally:
-            gc.enable()
-            gc.unfreeze()
-        return t_start.elapsed_time(t_end) / args.steps
-
     wanted = [m for m in args.schedules.split(",") if m]
     if any(m not in cra.MODES for m in wanted):
         print(f"--schedules takes names from {cra.MODES}", file=sys.stderr)
@@ -197,7 +384,9 @@ def main() -> int:
     order = [m for m in ("merge", "accum") if m in wanted] + ["stream"]
     schedules = {}
     for mode in order:   # the step's own schedule last, on a warm GPU
-        ms = timed(mode)
+        ms = timed_steps(lambda i, m=mode: share_step(m, spare_attn if i is False else attn_ev[m][i],
+                                                      spare_merge if i is False else merge_ev[i]),
+                         args.steps, args.warmup, stream, ev)
         launches = 1 if mode == "stream" else nch
         a_ms = sum(row[c][0].elapsed_time(row[c][1]) for row in attn_ev[mode]
                    for c in range(launches)) / (args.steps * launches)
@@ -207,10 +396,9 @@ def main() -> int:
                            "attn_avg_launch_us": round(a_ms * 1e3, 2)}
     ms_step = schedules["stream"]["ms_per_step"]
     value = flops_step / (ms_step / 1e3) / 1e12
-
     attn_avg_ms = schedules["stream"]["attn_avg_launch_us"] / 1e3
-    attn_flops_per_launch = flops_step
-    attn_tflops = attn_flops_per_launch / (attn_avg_ms / 1e3) / 1e12
+    attn_tflops = flops_step / (attn_avg_ms / 1e3) / 1e12
+
     timed_merge = "merge" in schedules and n_merge > 0
     merge_ms = sum(a.elapsed_time(b) for row in merge_ev for a, b in row) if timed_merge else 0.0
     merge_avg_ms = merge_ms / max(1, args.steps * n_merge)
@@ -221,63 +409,12 @@ def main() -> int:
     if timed_merge:
         xa, xb = bufs.o_acc, bufs.o_part
         xc = torch.empty_like(xa)
-        for _ in range(3):
-            torch.add(xa, xb, out=xc)
-        torch.cuda.synchronize()
-        a0, a1 = ev(), ev()
-        a0.record(stream)
-        for _ in range(20):
-            torch.add(xa, xb, out=xc)
-        a1.record(stream)
-        torch.cuda.synchronize()
-        add_gbs = 3 * xa.numel() * 4 / (a0.elapsed_time(a1) / 20 / 1e3) / 1e9
+        add_ms = timed_steps(lambda i: torch.add(xa, xb, out=xc), 20, 3, stream, ev)
+        add_gbs = 3 * xa.numel() * 4 / (add_ms / 1e3) / 1e9
         del xc
 
-    backward = None
-    if not args.no_backward:
-        # Backward of the share in one pass (cpattn_bwd_chunks: dq and every chunk's dk, dv) from
-        # the share's forward (o, lse) and a synthetic gradient.
-        o_f, lse_f = bufs.o_acc, bufs.lse_acc
-        cra.cpattn_fwd_chunks(q, ks, vs, cu_q, cu_ks, q_off, k_offs, True, out=o_f, lse=lse_f,
-                              workspace=bufs.workspace, stream=stream)
-        gen = torch.Generator(device="cuda").manual_seed(args.seed + 1)
-        dout = torch.randn(q.shape, device="cuda", generator=gen).to(bf)
-        f32 = dict(dtype=torch.float32, device="cuda")
-        dq = torch.zeros(q.shape, **f32)
-        dks = [torch.zeros(k.shape, **f32) for k in ks]
-        dvs = [torch.zeros(v.shape, **f32) for v in vs]
-        bws = torch.empty(max(cra.cpattn_bwd_workspace_size_chunks(len(cu_q) - 1, cu_q, cu_ks,
-                                                                   w.hq, w.hkv, w.d), 256),
-                          dtype=torch.uint8, device="cuda")
-
-        def bwd_step():
-            cra.cpattn_bwd_chunks(q, ks, vs, o_f, lse_f, dout, cu_q, cu_ks, q_off, k_offs, True,
-                                  dq=dq, dks=dks, dvs=dvs, workspace=bws, stream=stream)
-
-        for _ in range(max(1, args.warmup)):
-            bwd_step()
-        torch.cuda.synchronize()
-        gc.collect()
-        gc.freeze()
-        gc.disable()
-        try:
-            b0, b1 = ev(), ev()
-            b0.record(stream)
-            for _ in range(args.steps):
-                bwd_step()
-            b1.record(stream)
-            torch.cuda.synchronize()
-        finally:
-            gc.enable()
-            gc.unfreeze()
-        bwd_ms = b0.elapsed_time(b1) / args.steps
-        bwd_flops = 10 * w.d * w.hq * sum(pairs_chunk)
-        backward = {"ms_per_step": round(bwd_ms, 4),
-                    "tflops": round(bwd_flops / (bwd_ms / 1e3) / 1e12, 2),
-                    "frac": round(bwd_flops / (bwd_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                    "flops_per_step": bwd_flops,
-                    "counted_as": "10 D Hq per visible pair (5 products of the forward's 2 D Hq)",
-                    "launches_per_step": "delta, dQ over all chunks, dK/dV over all chunks"}
+    backward = None if args.no_backward else time_backward(w, gg, args.steps, args.warmup, stream,
+                                                           ev, args.seed)
 
     # Other packs of the same workload (further seeds: same shapes, other sequence lengths), the
     # step timed the same way, and the aggregate over all of them (total FLOPs / total time).
@@ -291,55 +428,24 @@ def main() -> int:
         tot_flops, tot_ms = flops_step, ms_step
         for sd in sweep_list:
             w2 = wl.make(args.workload, sd)
-            g2 = w2.groups[0]
-            q2 = torch.from_numpy(g2.q).to("cuda", bf)
-            ks2 = [torch.from_numpy(c.k).to("cuda", bf) for c in g2.chunks]
-            vs2 = [torch.from_numpy(c.v).to("cuda", bf) for c in g2.chunks]
-            cu_q2 = np.ascontiguousarray(g2.cu_q, np.int32)
-            q_off2 = np.ascontiguousarray(g2.q_off, np.int32)
-            cu_ks2 = [np.ascontiguousarray(c.cu_k, np.int32) for c in g2.chunks]
-            k_offs2 = [np.ascontiguousarray(c.k_off, np.int32) for c in g2.chunks]
-            bufs2 = cra.ShareBuffers.allocate(q2, w2.hkv, cu_q2, len(g2.chunks))
-            flops2 = sum(4 * w2.d * w2.hq * visible_pairs(cu_q2, c.cu_k, q_off2, c.k_off)
-                         for c in g2.chunks)
-
-            def step2():
-                cra.cpattn_fwd_chunks(q2, ks2, vs2, cu_q2, cu_ks2, q_off2, k_offs2, True,
-                                      out=bufs2.o_acc, lse=bufs2.lse_acc, workspace=bufs2.workspace,
-                                      stream=stream)
-
-            for _ in range(args.warmup):
-                step2()
-            torch.cuda.synchronize()
-            gc.collect()
-            gc.freeze()
-            gc.disable()
-            try:
-                s0, s1 = ev(), ev()
-                s0.record(stream)
-                for _ in range(args.steps):
-                    step2()
-                s1.record(stream)
-                torch.cuda.synchronize()
-            finally:
-                gc.enable()
-                gc.unfreeze()
-            ms2 = s0.elapsed_time(s1) / args.steps
-            per_seed.append({"seed": sd, "pieces": [int(x) for x in np.diff(cu_q2)],
+            g2 = GpuGroup(w2, w2.groups[0])
+            ms2 = timed_steps(lambda i: g2.fwd(stream), args.steps, args.warmup, stream, ev)
+            per_seed.append({"seed": sd, "pieces": [int(x) for x in np.diff(g2.cu_q)],
                              "ms_per_step": round(ms2, 4),
-                             "tflops": round(flops2 / (ms2 / 1e3) / 1e12, 2)})
-            tot_flops += flops2
+                             "tflops": round(g2.flops / (ms2 / 1e3) / 1e12, 2)})
+            tot_flops += g2.flops
             tot_ms += ms2
-            del q2, ks2, vs2, bufs2
+            del g2
         seeds = {"per_seed": per_seed,
                  "aggregate_tflops": round(tot_flops / (tot_ms / 1e3) / 1e12, 2),
                  "aggregate_frac": round(tot_flops / (tot_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
-    import hashlib
-    with open(ATTN_SOURCE, "rb") as f:
-        traffic = PROFILED_TRAFFIC.get((args.workload, hashlib.sha256(f.read()).hexdigest()))
-    tk_all = sum(int(c[-1]) for c in cu_ks)
-    attn_bytes = tq * w.hq * w.d * 2 + 2 * tk_all * w.hkv * w.d * 2 + tq * w.hq * w.d * 4 + tq * w.hq * 4
+    others = {}
+    for name in [x for x in args.other_workloads.split(",") if x.strip()]:
+        others[name] = time_workload(name, args.seed, args.steps, args.warmup, stream, ev,
+                                     backward=not args.no_backward and name == "ctx128k_share")
+        torch.cuda.empty_cache()
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -353,31 +459,31 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name} (seed {w.seed}): last CP{nch} rank of "
-                               f"{pack_words(w.lengths)}, local Q {tq} tokens in "
-                               f"{len(cu_q) - 1} sequences, {nch} KV chunks of "
-                               f"{int(cu_ks[0][-1])} tokens, {w.hq}/{w.hkv} heads, D={w.d}, causal",
+        "config": {"workload": describe(w),
                    "global_batch": int(sum(w.lengths)), "seq_len": int(max(w.lengths)),
                    "parallelism": f"cp{nch}-share"},
         "mfma_util": round(value / BF16_PEAK_TFLOPS, 4),
+        "tokens_per_step": {"query": tq, "key": gg.tk},
+        "query_tokens_per_s": round(tq / (ms_step / 1e3), 1),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic,
+                     "traffic": stored_traffic(args.workload),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)",
-                     "algorithmic_bytes_per_launch": attn_bytes,
+                     "algorithmic_bytes_per_launch": gg.alg_bytes,
                      "kernel": "attn_fwd_bf16_kernel<128,false> over all chunks (event-timed per "
-                               "cpattn_fwd_chunks call)",
+                               "cpattn_fwd_chunks call, plan upload included)",
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
-                     "flops_per_launch": attn_flops_per_launch},
+                     "flops_per_launch": flops_step},
         "schedules": schedules,
         "seeds": seeds,
         "backward": backward,
+        "workloads": others,
         "merge": {"schedule": "merge", "avg_launch_us": round(merge_avg_ms * 1e3, 2) if timed_merge else None,
                   "bytes_per_launch": merge_bytes, "achieved_GBs": round(merge_gbs, 1) if merge_gbs else None,
                   "hbm_frac": round(merge_gbs / HBM_PEAK_GBS, 4) if merge_gbs else None,
                   "torch_add_same_bytes_GBs": round(add_gbs, 1) if add_gbs else None},
         "flops_per_step": flops_step,
-        "cpu_baseline": None,
+        "cpu_baseline": cb,
     }
     if args.copy_calibration:
         # A plain elementwise copy of known size whose source is not cache-resident:
@@ -409,10 +515,6 @@ def main() -> int:
         for _ in range(20):
             dcp_schedule_ref(dcp_lens, 8, 4096)
         result["dcp_schedule"]["oracle_host_us_per_call"] = round((time.perf_counter() - t0) / 20 * 1e6, 1)
-        cb = cpu_baseline(w, g)
-        cb["value"] = float(f"{cb['value']:.4g}")
-        cb.pop("seconds", None)
-        result["cpu_baseline"] = cb
     print(json.dumps(result))
     return 0
 

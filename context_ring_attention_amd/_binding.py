@@ -240,6 +240,24 @@ def _check_tensor(name, t):
         raise ValueError(f"{name} must be a contiguous CUDA tensor")
 
 
+def _on_device(name, t, device):
+    """A caller-supplied output or workspace must live on q's GPU: the kernels write through
+    its pointer, and a host pointer handed to a kernel faults the GPU."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a CUDA tensor on {device} (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(workspace, need: int, device):
+    """The caller's workspace (checked) or a fresh one; returns (tensor, bytes)."""
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    _on_device("workspace", workspace, device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def _outputs(q, out, lse):
     import torch
     tq, hq, d = q.shape
@@ -247,6 +265,8 @@ def _outputs(q, out, lse):
         out = torch.empty((tq, hq, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _on_device("out", out, q.device)
+    _on_device("lse", lse, q.device)
     if out.shape != (tq, hq, d) or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 [Tq, Hq, D] tensor")
     if lse.shape != (hq, tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -274,14 +294,16 @@ def _fwd_one(fn_name, q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_o
         raise ValueError("k and v must be [Tk, Hkv, D] with Q's D")
     if int(cq[-1]) != tq or int(ck[-1]) != tk:
         raise ValueError("cu_seqlens must end at the row counts of q and k")
+    for name, t in (("k", k), ("v", v)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device {q.device}")
     out, lse = _outputs(q, out, lse)
     need = lib.cpattn_workspace_size(nseq, pq, hq, hkv, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
     _check(getattr(lib, fn_name)(c_void_p(q.data_ptr()), c_void_p(k.data_ptr()),
                                  c_void_p(v.data_ptr()), pq, pk, pqo, pko, nseq, hq, hkv, d, dt,
                                  int(causal), c_void_p(out.data_ptr()), c_void_p(lse.data_ptr()),
-                                 c_void_p(workspace.data_ptr()), workspace.numel(),
+                                 c_void_p(workspace.data_ptr()), ws_bytes,
                                  _stream_handle(stream)))
     return out, lse
 
@@ -346,20 +368,21 @@ def cpattn_fwd_chunks(q, ks: Sequence, vs: Sequence, cu_seqlens_q, cu_seqlens_ks
         hkv = ks[c].shape[1]
         if int(ck[c, -1]) != ks[c].shape[0]:
             raise ValueError(f"cu_seqlens_ks[{c}] must end at chunk {c}'s row count")
+        if ks[c].device != q.device or vs[c].device != q.device:
+            raise ValueError(f"chunk {c}'s k and v must be on q's device {q.device}")
     if hkv is None:
         raise ValueError("need at least one chunk")
     if accumulate and (out is None or lse is None):
         raise ValueError("accumulate=True folds into existing out and lse tensors")
     out, lse = _outputs(q, out, lse)
     need = lib.cpattn_workspace_size_chunks(nseq, pq, hq, hkv, d, nch)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
     kp = (c_void_p * max(nch, 1))(*[t.data_ptr() for t in ks])
     vp = (c_void_p * max(nch, 1))(*[t.data_ptr() for t in vs])
     _check(lib.cpattn_fwd_chunks(c_void_p(q.data_ptr()), kp, vp, nch, pq, _ptr(ck), pqo, _ptr(ko),
                                  nseq, hq, hkv, d, dt, int(causal), int(accumulate),
                                  c_void_p(out.data_ptr()), c_void_p(lse.data_ptr()),
-                                 c_void_p(workspace.data_ptr()), workspace.numel(),
+                                 c_void_p(workspace.data_ptr()), ws_bytes,
                                  _stream_handle(stream)))
     return out, lse
 
@@ -409,18 +432,21 @@ def cpattn_bwd_chunk(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, q_pos_offs
     dq = torch.zeros((tq, hq, d), **f32) if dq is None else dq
     dk = torch.zeros((tk, hkv, d), **f32) if dk is None else dk
     dv = torch.zeros((tk, hkv, d), **f32) if dv is None else dv
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do), ("lse", lse)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device {q.device}")
     for name, t, shp in (("dq", dq, (tq, hq, d)), ("dk", dk, (tk, hkv, d)), ("dv", dv, (tk, hkv, d))):
+        _on_device(name, t, q.device)
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shp:
             raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shp}")
     need = lib.cpattn_bwd_workspace_size(nseq, pq, pk, hq, hkv, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
     _check(lib.cpattn_bwd_chunk(c_void_p(q.data_ptr()), c_void_p(k.data_ptr()),
                                 c_void_p(v.data_ptr()), c_void_p(o.data_ptr()),
                                 c_void_p(do.data_ptr()), c_void_p(lse.data_ptr()), pq, pk, pqo, pko,
                                 nseq, hq, hkv, d, dt, int(causal), c_void_p(dq.data_ptr()),
                                 c_void_p(dk.data_ptr()), c_void_p(dv.data_ptr()),
-                                c_void_p(workspace.data_ptr()), workspace.numel(),
+                                c_void_p(workspace.data_ptr()), ws_bytes,
                                 _stream_handle(stream)))
     return dq, dk, dv
 
@@ -478,21 +504,29 @@ def cpattn_bwd_chunks(q, ks: Sequence, vs: Sequence, o, lse, do, cu_seqlens_q,
     dq = torch.zeros((tq, hq, d), **f32) if dq is None else dq
     dks = [torch.zeros(t.shape, **f32) for t in ks] if dks is None else list(dks)
     dvs = [torch.zeros(t.shape, **f32) for t in vs] if dvs is None else list(dvs)
+    for name, t in (("o", o), ("do", do), ("lse", lse)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device {q.device}")
+    if len(dks) != nch or len(dvs) != nch:
+        raise ValueError("dks and dvs must have one entry per chunk")
+    _on_device("dq", dq, q.device)
     if dq.dtype != torch.float32 or not dq.is_contiguous() or tuple(dq.shape) != (tq, hq, d):
         raise ValueError("dq must be a contiguous float32 tensor like q")
     for c in range(nch):
+        if ks[c].device != q.device or vs[c].device != q.device:
+            raise ValueError(f"chunk {c}'s k and v must be on q's device {q.device}")
         for name, t in (("dks", dks[c]), ("dvs", dvs[c])):
+            _on_device(f"{name}[{c}]", t, q.device)
             if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != ks[c].shape:
                 raise ValueError(f"{name}[{c}] must be a contiguous float32 tensor like ks[{c}]")
     need = lib.cpattn_bwd_workspace_size_chunks(nseq, pq, _ptr(ck), nch, hq, hkv, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
     arr = lambda ts: (c_void_p * max(nch, 1))(*[t.data_ptr() for t in ts])
     _check(lib.cpattn_bwd_chunks(c_void_p(q.data_ptr()), arr(ks), arr(vs), nch,
                                  c_void_p(o.data_ptr()), c_void_p(do.data_ptr()),
                                  c_void_p(lse.data_ptr()), pq, _ptr(ck), pqo, _ptr(ko), nseq, hq,
                                  hkv, d, dt, int(causal), c_void_p(dq.data_ptr()), arr(dks),
-                                 arr(dvs), c_void_p(workspace.data_ptr()), workspace.numel(),
+                                 arr(dvs), c_void_p(workspace.data_ptr()), ws_bytes,
                                  _stream_handle(stream)))
     return dq, dks, dvs
 
@@ -507,8 +541,9 @@ def cpattn_merge(o_a, lse_a, o_b, lse_b, stream=None) -> None:
     for name, x, shp in (("o_a", o_a, (t, hq, d)), ("o_b", o_b, (t, hq, d)),
                          ("lse_a", lse_a, (hq, t)), ("lse_b", lse_b, (hq, t))):
         if (not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous()
-                or tuple(x.shape) != shp):
-            raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape {shp}")
+                or tuple(x.shape) != shp or x.device != o_a.device):
+            raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape {shp} "
+                             f"on {o_a.device}")
     _check(lib.cpattn_merge(c_void_p(o_a.data_ptr()), c_void_p(lse_a.data_ptr()),
                             c_void_p(o_b.data_ptr()), c_void_p(lse_b.data_ptr()), t, hq, d,
                             _stream_handle(stream)))

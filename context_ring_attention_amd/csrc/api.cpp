@@ -1,8 +1,6 @@
 // C ABI of libcpattn: argument checks, plan upload, kernel dispatch.
 #include <algorithm>
 #include <cstring>
-#include <deque>
-#include <mutex>
 #include <vector>
 
 #include "internal.h"
@@ -13,83 +11,26 @@ void clear_error();
 
 namespace {
 
-// Plans are built on the host into a pinned host ring that the library owns (one per device,
-// created on first use and kept for the life of the process), and the kernels read them from
-// there directly: a work-group reads its few plan records once, and no copy sits between
-// consecutive launches on the stream.  A region of the ring is reused only after the event
-// recorded behind the launches that read it has completed; in steady state those launches
-// finished long ago and the check returns at once.
-class StagingRing {
- public:
-  static constexpr size_t kCapacity = size_t(8) << 20;
-  static constexpr size_t kAlign = 256;
-
-  // Write `bytes` with `fill` into a free region of the ring, then `launch(region)` enqueues on
-  // `stream` the kernels that read it; the region is held until they have run.
-  template <class Fill, class Launch>
-  cpattn_status run(size_t bytes, hipStream_t stream, Fill&& fill, Launch&& launch) {
-    std::lock_guard<std::mutex> lock(mu_);
-    if (!host_) {
-      // Coherent (fine-grained) host memory: the GPU never serves a kernel's read of a reused
-      // region from a cache line filled by an earlier launch.
-      if (hipHostMalloc(&host_, kCapacity, hipHostMallocCoherent) != hipSuccess) {
-        host_ = nullptr;
-        return set_error(CPATTN_ERR_HIP, "hipHostMalloc of the plan staging ring failed");
-      }
-    }
-    if (bytes > kCapacity)
-      return set_error(CPATTN_ERR_UNSUPPORTED, "plan of %zu bytes exceeds the staging ring", bytes);
-    size_t begin = head_;
-    if (begin + bytes > kCapacity) begin = 0;
-    const size_t end = begin + bytes;
-    // Wait for every earlier copy that read [begin, end); drop finished fences.
-    for (auto it = fences_.begin(); it != fences_.end();) {
-      const bool overlap = it->begin < end && begin < it->end;
-      if (overlap) {
-        if (hipEventSynchronize(it->ev) != hipSuccess)
-          return set_error(CPATTN_ERR_HIP, "hipEventSynchronize on the staging ring failed");
-      }
-      if (overlap || hipEventQuery(it->ev) == hipSuccess) {
-        spare_.push_back(it->ev);
-        it = fences_.erase(it);
-      } else {
-        ++it;
-      }
-    }
-    char* src = static_cast<char*>(host_) + begin;
-    fill(src);
-    const cpattn_status st = launch(static_cast<const char*>(src));
-    if (st != CPATTN_OK) return st;  // nothing was enqueued: the region stays free
-    hipEvent_t ev;
-    if (!spare_.empty()) {
-      ev = spare_.back();
-      spare_.pop_back();
-    } else if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
-      return set_error(CPATTN_ERR_HIP, "hipEventCreate failed");
-    }
-    if (hipEventRecord(ev, stream) != hipSuccess) {
-      spare_.push_back(ev);
-      return set_error(CPATTN_ERR_HIP, "hipEventRecord failed");
-    }
-    fences_.push_back(Fence{begin, end, ev});
-    head_ = (end + kAlign - 1) / kAlign * kAlign;
-    return CPATTN_OK;
-  }
-
- private:
-  struct Fence {
-    size_t begin, end;
-    hipEvent_t ev;
-  };
-  std::mutex mu_;
-  void* host_ = nullptr;
-  size_t head_ = 0;
-  std::deque<Fence> fences_;
-  std::vector<hipEvent_t> spare_;
-};
-
-constexpr int kMaxDevices = 64;
-StagingRing g_rings[kMaxDevices];
+// Every call builds its plan on the host and copies it into the caller's device workspace on
+// the caller's stream, ahead of the launches that read it; the library holds no memory and no
+// state between calls.  The host copy is pageable: the runtime has taken the bytes when
+// hipMemcpyAsync returns, so the buffer can go at once.  A stream being captured into a graph
+// is refused, since a captured copy would re-read that freed host buffer on every replay.
+cpattn_status stage_plan(void* dst, const std::vector<char>& host, hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess)
+    return set_error(CPATTN_ERR_HIP, "hipStreamIsCapturing failed");
+  if (cap != hipStreamCaptureStatusNone)
+    return set_error(CPATTN_ERR_UNSUPPORTED,
+                     "the stream is being captured: the plan upload reads host memory that is "
+                     "freed when the call returns");
+  if (host.empty()) return CPATTN_OK;
+  const hipError_t err =
+      hipMemcpyAsync(dst, host.data(), host.size(), hipMemcpyHostToDevice, stream);
+  if (err != hipSuccess)
+    return set_error(CPATTN_ERR_HIP, "plan upload failed: %s", hipGetErrorString(err));
+  return CPATTN_OK;
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -236,38 +177,45 @@ cpattn_status fwd_impl(const void* q, const void* const* ks, const void* const* 
   if (n * head_groups > int64_t(INT32_MAX) || n * nchunks > int64_t(INT32_MAX))
     return set_error(CPATTN_ERR_UNSUPPORTED, "too many tiles for one launch");
 
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return set_error(CPATTN_ERR_HIP, "hipGetDevice failed");
-  auto fill = [&](char* dst) {
-    build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal,
-                  g, reinterpret_cast<cpattn_plan_entry*>(dst), n, nullptr);
-  };
-  auto launch = [&](const char* staged) -> cpattn_status {
-    const auto* plan = reinterpret_cast<const cpattn_plan_entry*>(staged);
-    hipError_t err;
-    if (dtype == CPATTN_BF16) {
-      ChunkPtrs<__bf16> kv{};
-      for (int32_t c = 0; c < nchunks; ++c) {
-        kv.k[c] = static_cast<const __bf16*>(ks[c]);
-        kv.v[c] = static_cast<const __bf16*>(vs[c]);
-      }
-      err = launch_attn_fwd_bf16(q, kv, nchunks, plan, int(n), head_groups, g.heads_per_tile, hq,
-                                 hkv, d, int(tq), accumulate != 0, o, lse, stream);
-    } else {
-      ChunkPtrs<float> kv{};
-      for (int32_t c = 0; c < nchunks; ++c) {
-        kv.k[c] = static_cast<const float*>(ks[c]);
-        kv.v[c] = static_cast<const float*>(vs[c]);
-      }
-      err = launch_attn_fwd_f32(static_cast<const float*>(q), kv, nchunks, plan, int(n), hq, hkv, d,
-                                int(tq), accumulate != 0, o, lse, stream);
+  // The plan region of the workspace is written by the upload: it must not overlap a tensor.
+  if (overlaps(workspace, plan_bytes, q, q_bytes) || overlaps(workspace, plan_bytes, o, o_bytes) ||
+      overlaps(workspace, plan_bytes, lse, lse_bytes))
+    return set_error(CPATTN_ERR_INVALID_ARG, "the workspace must not overlap q, o or lse");
+  for (int32_t c = 0; c < nchunks; ++c) {
+    const int64_t tk = cu_seqlens_k[int64_t(c) * (nseq + 1) + nseq];
+    const size_t kv_bytes = size_t(tk) * hkv * d * esz;
+    if (overlaps(workspace, plan_bytes, ks[c], kv_bytes) ||
+        overlaps(workspace, plan_bytes, vs[c], kv_bytes))
+      return set_error(CPATTN_ERR_INVALID_ARG, "the workspace must not overlap k or v (chunk %d)", c);
+  }
+
+  std::vector<char> host(plan_bytes);
+  build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal, g,
+                reinterpret_cast<cpattn_plan_entry*>(host.data()), n, nullptr);
+  st = stage_plan(workspace, host, stream);
+  if (st != CPATTN_OK) return st;
+  const auto* plan = static_cast<const cpattn_plan_entry*>(workspace);
+  hipError_t err;
+  if (dtype == CPATTN_BF16) {
+    ChunkPtrs<__bf16> kv{};
+    for (int32_t c = 0; c < nchunks; ++c) {
+      kv.k[c] = static_cast<const __bf16*>(ks[c]);
+      kv.v[c] = static_cast<const __bf16*>(vs[c]);
     }
-    if (err != hipSuccess)
-      return set_error(CPATTN_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
-    return CPATTN_OK;
-  };
-  return g_rings[dev].run(plan_bytes, stream, fill, launch);
+    err = launch_attn_fwd_bf16(q, kv, nchunks, plan, int(n), head_groups, g.heads_per_tile, hq,
+                               hkv, d, int(tq), accumulate != 0, o, lse, stream);
+  } else {
+    ChunkPtrs<float> kv{};
+    for (int32_t c = 0; c < nchunks; ++c) {
+      kv.k[c] = static_cast<const float*>(ks[c]);
+      kv.v[c] = static_cast<const float*>(vs[c]);
+    }
+    err = launch_attn_fwd_f32(static_cast<const float*>(q), kv, nchunks, plan, int(n), hq, hkv, d,
+                              int(tq), accumulate != 0, o, lse, stream);
+  }
+  if (err != hipSuccess)
+    return set_error(CPATTN_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
+  return CPATTN_OK;
 }
 
 }  // namespace
@@ -308,12 +256,12 @@ cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void
 namespace {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// The two plans are staged in the pinned ring (query plan, then key plan at key_plan_at);
-// the device workspace holds delta and the log2-scaled LSE.
+// Workspace of the backward: the query plan, the key plan (both uploaded by the call), then
+// delta and the log2-scaled LSE (written by the delta kernel), each 256-byte aligned.
 struct BwdLayout {
-  int64_t n_q, n_k;        // tiles of the query plan and of the key plan
-  size_t key_plan_at, plan_bytes;  // in the staging ring
-  size_t delta_at, lse2_at, total; // in the workspace
+  int64_t n_q, n_k;                 // entries of the query plan and tiles of the key plan
+  size_t key_plan_at, plan_bytes;   // plans: [0, plan_bytes)
+  size_t delta_at, lse2_at, total;
 };
 
 BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq) {
@@ -321,8 +269,8 @@ BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq) {
   l.n_q = n_q;
   l.n_k = n_k;
   l.key_plan_at = align256(size_t(n_q) * sizeof(cpattn_plan_entry));
-  l.plan_bytes = l.key_plan_at + size_t(n_k) * sizeof(cpattn_plan_entry);
-  l.delta_at = 0;
+  l.plan_bytes = l.key_plan_at + size_t(n_k) * sizeof(KeyTile);
+  l.delta_at = align256(l.plan_bytes);
   l.lse2_at = align256(l.delta_at + size_t(tq) * hq * sizeof(float));
   l.total = std::max<size_t>(256, l.lse2_at + size_t(tq) * hq * sizeof(float));
   return l;
@@ -419,15 +367,19 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
     if (overlaps(out_p[a], out_b[a], ws, lay.total))
       return set_error(CPATTN_ERR_INVALID_ARG, "the workspace must not overlap the gradients");
 
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return set_error(CPATTN_ERR_HIP, "hipGetDevice failed");
-  auto fill = [&](char* dst) {
-    build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal, g,
-                  reinterpret_cast<cpattn_plan_entry*>(dst), n_qt, nullptr);
-    build_key_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq,
-                      causal, reinterpret_cast<KeyTile*>(dst + lay.key_plan_at), lay.n_k);
-  };
+  for (size_t b = 0; b < in_p.size(); ++b)
+    if (overlaps(in_p[b], in_b[b], ws, lay.total))
+      return set_error(CPATTN_ERR_INVALID_ARG, "the workspace must not overlap an input");
+
+  std::vector<char> host(lay.plan_bytes);
+  build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal, g,
+                reinterpret_cast<cpattn_plan_entry*>(host.data()), n_qt, nullptr);
+  build_key_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal,
+                    reinterpret_cast<KeyTile*>(host.data() + lay.key_plan_at), lay.n_k);
+  st = stage_plan(ws, host, stream);
+  if (st != CPATTN_OK) return st;
+  const auto* qplan = reinterpret_cast<const cpattn_plan_entry*>(ws);
+  const auto* kplan = reinterpret_cast<const KeyTile*>(ws + lay.key_plan_at);
   float* delta = reinterpret_cast<float*>(ws + lay.delta_at);
   float* lse2 = reinterpret_cast<float*>(ws + lay.lse2_at);
   ChunkPtrs<__bf16> kv{};
@@ -438,21 +390,16 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
     dkv.k[c] = dks[c];
     dkv.v[c] = dvs[c];
   }
-  auto launch = [&](const char* staged) -> cpattn_status {
-    const auto* qplan = reinterpret_cast<const cpattn_plan_entry*>(staged);
-    const auto* kplan = reinterpret_cast<const KeyTile*>(staged + lay.key_plan_at);
-    hipError_t err = launch_bwd_delta(do_, o, lse, int(tq), hq, d, delta, lse2, stream);
-    if (err == hipSuccess)
-      err = launch_bwd_dq(q, kv, nchunks, do_, lse, delta, qplan, int(n_qt), head_groups,
-                          g.heads_per_tile, hq, hkv, d, int(tq), dq, stream);
-    if (err == hipSuccess)
-      err = launch_bwd_dkdv(q, kv, do_, lse2, delta, kplan, int(lay.n_k), hq, hkv, d, int(tq), dkv,
-                            stream);
-    if (err != hipSuccess)
-      return set_error(CPATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
-    return CPATTN_OK;
-  };
-  return g_rings[dev].run(lay.plan_bytes, stream, fill, launch);
+  hipError_t err = launch_bwd_delta(do_, o, lse, int(tq), hq, d, delta, lse2, stream);
+  if (err == hipSuccess)
+    err = launch_bwd_dq(q, kv, nchunks, do_, lse, delta, qplan, int(n_qt), head_groups,
+                        g.heads_per_tile, hq, hkv, d, int(tq), dq, stream);
+  if (err == hipSuccess)
+    err = launch_bwd_dkdv(q, kv, do_, lse2, delta, kplan, int(lay.n_k), hq, hkv, d, int(tq), dkv,
+                          stream);
+  if (err != hipSuccess)
+    return set_error(CPATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
+  return CPATTN_OK;
 }
 
 cpattn_status cpattn_bwd_chunk(const void* q, const void* k, const void* v, const float* o,

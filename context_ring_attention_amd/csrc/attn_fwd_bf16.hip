@@ -10,8 +10,8 @@
 // writes the normalised O = acc / l and LSE = m + ln l of the tile's rows over
 // all those keys.  With one chunk that is the partial of that chunk.  In
 // accumulate mode the epilogue instead folds (O, LSE) into the running result
-// already in memory with the pages' merge (alpha, beta weights of the two
-// sides), so a ring step needs no separate merge pass.
+// already in memory with the merge of two partials (each side weighted by its
+// share of the softmax mass), so a ring step needs no separate merge pass.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64): the score tile is
 // computed transposed, S^T[key][token] = K * Q^T, so the 32x32 accumulator puts
@@ -42,13 +42,15 @@
 // O / l cancels the common factor exactly.  This skips the 64-register rescale
 // of the accumulator on almost every block.
 //
-// Row sums are taken on the bf16-rounded P with v_dot2_f32_bf16 (two keys per
-// instruction), so l sums exactly the weights the PV product multiplies.  Most
-// blocks skip the row max altogether: once a reference max is set, P is formed
-// against it directly, and a lane sum <= 2^8 proves no score passed the
-// threshold (every p >= 0), which is all the max was needed for; otherwise the
-// block is redone with the max (and rescale) first.  Both paths give the same
-// bits as always taking the max.
+// Row sums are taken over the fp32 probabilities, before they are rounded to
+// bf16 for the PV product, so the LSE carries only fp32 rounding (a sum over
+// the rounded values would be off by up to 2^-9 of each term, which for rows
+// with few visible keys moves the LSE by more than 1e-3).  Most blocks skip the
+// row max altogether: once a reference max is set, P is formed against it
+// directly, and a lane sum <= 2^8 proves no score passed the threshold (every
+// p >= 0), which is all the max was needed for; otherwise the block is redone
+// with the max (and rescale) first.  Both paths give the same bits as always
+// taking the max.
 //
 // Scheduling: the two waves of a SIMD (one from each of the CU's two
 // work-groups) run the same block loop; a wave raises its issue priority for
@@ -70,7 +72,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -295,22 +296,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         // tile kk / 2) and this lane's sum of them.
         bf16x8 pf[4];
         auto exp_block = [&](float neg) {
+          float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
-            pf[0][jj] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[jj], scale_log2, neg));
-            pf[1][jj] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[8 + jj], scale_log2, neg));
-            pf[2][jj] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[jj], scale_log2, neg));
-            pf[3][jj] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[8 + jj], scale_log2, neg));
-          }
-          const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-          float part[4];
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            part[kk] = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              part[kk] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[kk][2 * i], pf[kk][2 * i + 1]},
-                                                         ones, part[kk], false);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[jj], scale_log2, neg));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[8 + jj], scale_log2, neg));
+            const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[jj], scale_log2, neg));
+            const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[8 + jj], scale_log2, neg));
+            pf[0][jj] = (__bf16)p0;
+            pf[1][jj] = (__bf16)p1;
+            pf[2][jj] = (__bf16)p2;
+            pf[3][jj] = (__bf16)p3;
+            part[0] += p0;
+            part[1] += p1;
+            part[2] += p2;
+            part[3] += p3;
           }
           return (part[0] + part[1]) + (part[2] + part[3]);
         };
@@ -389,11 +389,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         write = false;
       } else if (lse_old != -INFINITY) {
         const float mm = fmaxf(lse_old, lse_new);
-        const float alpha = expf(lse_old - mm), beta = expf(lse_new - mm);
-        const float inv = 1.0f / (alpha + beta);
-        wa = alpha * inv;
-        wb = beta * inv / l_tot;
-        lse_out = mm + logf(alpha + beta);
+        const float ea = expf(lse_old - mm), eb = expf(lse_new - mm);
+        const float inv = 1.0f / (ea + eb);
+        wa = ea * inv;
+        wb = eb * inv / l_tot;
+        lse_out = mm + logf(ea + eb);
       }
     }
     if (write) {

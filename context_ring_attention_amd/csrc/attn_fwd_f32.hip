@@ -139,11 +139,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
         write = false;
       } else if (lse_old != -INFINITY) {
         const float mm = fmaxf(lse_old, lse_new);
-        const float alpha = expf(lse_old - mm), beta = expf(lse_new - mm);
-        const float inv = 1.0f / (alpha + beta);
-        wa = alpha * inv;
-        wb = beta * inv;
-        lse_out = mm + logf(alpha + beta);
+        const float ea = expf(lse_old - mm), eb = expf(lse_new - mm);
+        const float inv = 1.0f / (ea + eb);
+        wa = ea * inv;
+        wb = eb * inv;
+        lse_out = mm + logf(ea + eb);
       }
     }
     if (write) {

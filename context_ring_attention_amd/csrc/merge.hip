@@ -1,12 +1,14 @@
 // LSE merge of two normalised partial attention results (HBM-bound).
 //
-// The pages' update ("Megatron 6D parallelism guide", section 6) keeps an
-// unnormalised accumulator with running max m and running sum l:
-//     m_new = max(m, m_step); alpha = exp(m - m_new); beta = exp(m_step - m_new)
-//     l = alpha*l + beta*l_step;  O = alpha*O + beta*O_step
-// For normalised partials (O, LSE) take m = LSE and l = 1; then the merged
-// partial is O = (alpha*O_a + beta*O_b) / (alpha + beta) with
-// LSE = m_new + ln(alpha + beta).  One of alpha, beta is exactly 1.
+// A normalised partial over a key set U is O = sum_u e^{s_u} v_u / sum_u e^{s_u} with
+// LSE = ln sum_u e^{s_u}.  Two partials over disjoint key sets combine into the
+// partial over their union: its LSE is ln(e^{lse_a} + e^{lse_b}), and its O mixes
+// the two sides, each weighted by its share of the union's softmax mass,
+// w_side = exp(lse_side - lse).  This is the combination step of the ring loop
+// ("Megatron 6D parallelism guide", section 6) written for normalised partials.
+// It is evaluated against mx = max(lse_a, lse_b): with ea = exp(lse_a - mx) and
+// eb = exp(lse_b - mx) (one of them exactly 1), lse = mx + ln(ea + eb) and
+// w_a = ea / (ea + eb), w_b = eb / (ea + eb).
 //
 // Layout: o [t, hq, d] fp32 (row (tok, h) is contiguous), lse [hq, t] fp32.
 // Each thread owns one float4 of a row; a row's d/4 threads sit in one wave
@@ -32,15 +34,15 @@ __device__ __forceinline__ void merge_row_chunk(float4* __restrict__ oa, const f
     return;
   }
   const float4 a = *oa;
-  const float m = fmaxf(la, lb);
-  const float alpha = expf(la - m);
-  const float beta = expf(lb - m);
-  const float l = alpha + beta;
-  const float inv = 1.0f / l;
-  const float wa = alpha * inv, wb = beta * inv;
+  const float mx = fmaxf(la, lb);
+  const float ea = expf(la - mx);
+  const float eb = expf(lb - mx);
+  const float mass = ea + eb;
+  const float inv = 1.0f / mass;
+  const float wa = ea * inv, wb = eb * inv;
   out = make_float4(wa * a.x + wb * b.x, wa * a.y + wb * b.y, wa * a.z + wb * b.z,
                     wa * a.w + wb * b.w);
-  lse_out = m + logf(l);
+  lse_out = mx + logf(mass);
   write = true;
 }
 

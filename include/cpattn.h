@@ -4,10 +4,10 @@
  *
  * This is the per-GPU compute of ring-style context parallelism as described in
  * the "Megatron 6D parallelism guide", section 6 (context parallelism): each
- * rank holds a slice S/CP of a sequence's queries, computes a flash-attention
- * partial result against one KV chunk at a time, and folds each partial into a
- * running result by the online-softmax update (running max m, running sum l,
- * rescale factors alpha and beta), returning O / l at the end.  Inputs are
+ * rank holds a 1/CP slice of a sequence's queries, computes a partial attention
+ * result against one KV chunk at a time, and folds each partial into a running
+ * result by the online-softmax rule (both sides rescaled to a common maximum,
+ * then added), normalising at the end.  Inputs are
  * "remove-padding / THD" packs (verl docs, "Dynamic Context Parallelism"): the
  * sequences of a micro-batch are concatenated without padding and described by
  * prefix sums of their lengths (cu_seqlens).
@@ -59,16 +59,20 @@ typedef enum {
 
 /*
  * Bytes of device workspace one cpattn_fwd_chunk call takes for these query
- * sequences (the size of the call's work plan, which is staged as described below).  cu_seqlens_q is host int32 [nseq + 1].  The
- * value depends only on nseq, the query lengths and the head counts, so one
- * workspace serves every KV chunk of a rank's share.  Returns 0 if the arguments
- * are invalid (nseq < 0, null cu_seqlens_q with nseq > 0, hq or hkv < 1).
+ * sequences: the size of the call's work plan.  cu_seqlens_q is host int32
+ * [nseq + 1].  The value depends only on nseq, the query lengths and the head
+ * counts, so one workspace serves every KV chunk of a rank's share.  Returns 0 if
+ * the arguments are invalid (nseq < 0, null cu_seqlens_q with nseq > 0, hq or
+ * hkv < 1).
  *
- * Work plans: every call builds its plan on the host into a pinned host ring that
- * the library allocates once per device (8 MiB, kept for the life of the process)
- * and the kernels read it from there; a region of the ring is reused only after
- * the launches that read it have completed.  The forward entry points validate
- * the workspace but do not write it (it is reserved for the library).
+ * Work plans: every call builds its plan on the host and copies it into the
+ * first bytes of the caller's workspace on `stream`, ahead of the kernels that
+ * read it.  The library allocates nothing and keeps no state between calls;
+ * consecutive calls on one stream may reuse one workspace (stream order keeps a
+ * plan until its kernels have run).  Calls on different streams need different
+ * workspaces.  A stream that is being captured into a graph is refused
+ * (CPATTN_ERR_UNSUPPORTED): the upload reads a host buffer that is freed when the
+ * call returns.
  */
 size_t cpattn_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q, int32_t hq, int32_t hkv,
                              int32_t d);
@@ -86,11 +90,11 @@ size_t cpattn_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_q, i
                                     int32_t hkv, int32_t d, int32_t nchunks);
 
 /*
- * One KV chunk: the flash-attention partial of the pages' ring loop
- * ("Megatron 6D parallelism guide", section 6, the per-step call that returns
- * O_step, m_step, l_step), returned in normalised form:
- *     o   [Tq, hq, d] fp32 = O_step / l_step        (device, written)
- *     lse [hq, Tq]    fp32 = m_step + ln l_step     (device, written)
+ * One KV chunk: the per-step partial result of the ring loop ("Megatron 6D
+ * parallelism guide", section 6: one attention call per KV chunk, returning an
+ * unnormalised output with its row maximum and row sum), here in normalised form:
+ *     o   [Tq, hq, d] fp32 = softmax over the chunk's visible keys, times V
+ *     lse [hq, Tq]    fp32 = ln of the row's sum of exp(score) over those keys
  * with Tq = cu_seqlens_q[nseq].
  *
  *   q       device [Tq, hq, d], dtype            (read)
@@ -99,8 +103,8 @@ size_t cpattn_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_q, i
  *   q_pos_offset, k_pos_offset   host int32 [nseq], >= 0, or NULL for all zeros
  *   hq % hkv == 0; d in {64, 128}
  *   workspace        device, >= cpattn_workspace_size(...) bytes, 256-byte aligned;
- *                    owned by the caller, reserved for the library (see above);
- *                    consecutive calls on one stream may reuse it.
+ *                    owned by the caller; the call uploads its plan into it (see
+ *                    above); it must not overlap q, k, v, o or lse.
  * The caller owns every buffer; o must not overlap q, k or v.  Rows of o/lse for
  * queries of zero-length key sequences are written as (0, -inf).
  * Returns CPATTN_OK, or an error code with nothing enqueued.
@@ -117,7 +121,7 @@ cpattn_status cpattn_fwd_chunk(const void* q, const void* k, const void* v,
  * running result in the kernel's epilogue instead of being written out,
  *     (o, lse) <- merge((o, lse), partial of this chunk)
  * with the merge of cpattn_merge below ("Megatron 6D parallelism guide", section
- * 6: the online-softmax update applied once per ring step).  o and lse are read
+ * 6: the combination applied once per ring step).  o and lse are read
  * and written (device, same shapes as cpattn_fwd_chunk); a first call on a fresh
  * result starts from O = 0, LSE = -inf everywhere.  Rows the chunk shows no key
  * keep their values exactly; rows whose running LSE is -inf take the partial
@@ -180,8 +184,9 @@ cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void
  *   dq        device [Tq, hq, d] fp32; dk, dv device [Tk, hkv, d] fp32   (read and written)
  *   metadata  as cpattn_fwd_chunk (host); dtype must be CPATTN_BF16; d in {64, 128}
  *   workspace device, >= cpattn_bwd_workspace_size(...) bytes, 256-byte aligned; it holds
- *             delta and the log2-scaled LSE until the kernels have run (the plans are
- *             staged in the library's pinned ring, see cpattn_workspace_size)
+ *             the call's two plans (uploaded as for the forward, see
+ *             cpattn_workspace_size), then delta and the log2-scaled LSE, until the
+ *             kernels have run; it must not overlap any tensor
  * Rows whose LSE is -inf (no visible key in the share) contribute nothing.  No output may
  * overlap an input or another output.  Returns CPATTN_OK, or an error code with nothing
  * enqueued (CPATTN_ERR_UNSUPPORTED for fp32 inputs).
@@ -216,8 +221,9 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Bytes of device workspace one cpattn_bwd_chunk call needs (delta [hq, Tq] and the
- * LSE in log2 units [hq, Tq], fp32).  Returns 0 for invalid arguments.
+ * Bytes of device workspace one cpattn_bwd_chunk call needs (its query and key plans,
+ * delta [hq, Tq] and the LSE in log2 units [hq, Tq], fp32).  Returns 0 for invalid
+ * arguments.
  */
 size_t cpattn_bwd_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_k, int32_t hq, int32_t hkv, int32_t d);
@@ -228,10 +234,13 @@ size_t cpattn_bwd_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_
                                         int32_t hkv, int32_t d);
 
 /*
- * The online-softmax merge of the pages' ring loop ("Megatron 6D parallelism
- * guide", section 6: m_new = max(m, m_step), alpha = exp(m - m_new),
- * beta = exp(m_step - m_new), l = alpha*l + beta*l_step, O = alpha*O + beta*O_step),
- * written for normalised partials over disjoint key sets.  In place:
+ * The merge of two partial results over disjoint key sets, the combination step
+ * of the ring loop ("Megatron 6D parallelism guide", section 6: the running
+ * result is rescaled to a common maximum and summed with each step's partial).
+ * For normalised partials it reads
+ *     lse = ln(exp(lse_a) + exp(lse_b))
+ *     o   = exp(lse_a - lse) * o_a + exp(lse_b - lse) * o_b
+ * i.e. each side is weighted by its share of the total softmax mass.  In place:
  *     (o_a, lse_a) <- merge((o_a, lse_a), (o_b, lse_b))
  *   o_a, o_b     device fp32 [t, hq, d]
  *   lse_a, lse_b device fp32 [hq, t]

@@ -19,10 +19,9 @@ exactly, up to rounding order):
     empty U_t    -> O_t = 0, LSE_t = -inf
 
   Sources: "Megatron 6D parallelism guide", section 6 (context parallelism):
-  the ring_attention pseudocode computes, per KV chunk, a flash-attention
-  partial (O_step, m_step, l_step), merges it into the running (O, m, l) by the
-  online-softmax update and returns O / l; that is exactly softmax(QK^T)V over
-  the union of the chunks.  The 1/sqrt(D) scale, the causal mask by global
+  the ring loop computes one attention partial per KV chunk, folds each into a
+  running result by rescaling both to a common maximum, and normalises at the
+  end; that is exactly softmax(QK^T)V over the union of the chunks.  The 1/sqrt(D) scale, the causal mask by global
   position, GQA and the LSE output are not printed on the pages; the readings
   taken are: scale 1/sqrt(D); mask inclusive of the diagonal (k_pos <= q_pos),
   never across sequences; contiguous GQA groups; LSE in natural log.
@@ -31,8 +30,9 @@ This is a two-pass softmax over whole rows (max first, then the sum), in row
 blocks only to bound memory.  It is not an online softmax and never splits a
 row's keys, so it shares neither code nor algorithm with the GPU kernels.
 
-merge_ref follows the pages' merge steps in their own notation (m_new, alpha,
-beta, l, O).
+merge_ref is the combination of two normalised partials over disjoint key sets,
+written from its definition: the union's LSE is the log of the summed softmax
+masses, and its O is the mass-weighted mix of the two sides.
 
 attention_bwd_ref is the gradient of the same function.  The pages train with
 context parallelism (a forward-backward pass per micro-batch); they print no
@@ -181,29 +181,25 @@ def attention_bwd_ref(q, k, v, do, cu_q, cu_k, q_off=None, k_off=None,
 def merge_ref(o_a, lse_a, o_b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
     """Merge two partial results over disjoint key sets (fp64).
 
-    Inputs are normalised partials: O [T, H, D] and LSE [H, T].  A normalised
-    partial (O, LSE) is the pages' unnormalised state with running max m = LSE,
-    running sum l = 1 and accumulator O.  The pages' update then reads
-        m_new = max(m_a, m_b); alpha = exp(m_a - m_new); beta = exp(m_b - m_new)
-        l = alpha * l_a + beta * l_b;  O = alpha * O_a + beta * O_b
-    and the result is normalised as O / l with LSE = m_new + ln l.  An empty
-    partial (LSE = -inf) is the identity; two empty partials give an empty one
-    (O = 0, LSE = -inf), never NaN.
+    Inputs are normalised partials: O [T, H, D] and LSE [H, T].  A normalised partial over
+    a key set U has mass exp(LSE) = sum_{u in U} exp(s_u) and O = sum_u exp(s_u) v_u / mass.
+    Over the union of two disjoint sets the mass is the sum of the two masses, so
+        LSE = ln(exp(lse_a) + exp(lse_b))
+        O   = exp(lse_a - LSE) * O_a + exp(lse_b - LSE) * O_b
+    (each side weighted by its share of the union's mass).  An empty partial (LSE = -inf,
+    mass 0) is the identity; two empty partials give an empty one (O = 0, LSE = -inf),
+    never NaN.
     """
     o_a = _as64(o_a); o_b = _as64(o_b)
-    m_a = _as64(lse_a).T[..., None]                 # [T, H, 1]
-    m_b = _as64(lse_b).T[..., None]
-    m_new = np.maximum(m_a, m_b)
-    both_empty = np.isneginf(m_new)
-    m_ref = np.where(both_empty, 0.0, m_new)
-    alpha = np.exp(m_a - m_ref)                      # exp(-inf) = 0 for an empty side
-    beta = np.exp(m_b - m_ref)
-    l = alpha * 1.0 + beta * 1.0
-    acc = np.where(alpha > 0, alpha * o_a, 0.0) + np.where(beta > 0, beta * o_b, 0.0)
-    l_safe = np.where(both_empty, 1.0, l)
-    o = np.where(both_empty, 0.0, acc / l_safe)
-    with np.errstate(divide="ignore"):
-        lse = np.where(both_empty, -np.inf, m_ref + np.log(l_safe))
+    la = _as64(lse_a).T[..., None]                  # [T, H, 1]
+    lb = _as64(lse_b).T[..., None]
+    lse = np.logaddexp(la, lb)                      # -inf only when both sides are empty
+    both_empty = np.isneginf(lse)
+    lse_safe = np.where(both_empty, 0.0, lse)
+    w_a = np.exp(la - lse_safe)                     # exp(-inf) = 0 for an empty side
+    w_b = np.exp(lb - lse_safe)
+    o = np.where(w_a > 0, w_a * o_a, 0.0) + np.where(w_b > 0, w_b * o_b, 0.0)
+    o = np.where(both_empty, 0.0, o)
     return o, lse[..., 0].T.copy()
 
 

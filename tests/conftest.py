@@ -22,3 +22,27 @@ def gpu_lib():
     import context_ring_attention_amd as cra
     cra.load()          # raises if libcpattn.so is not built
     return cra
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The achieved forward errors against the oracle, worst first, beside their bounds."""
+    try:
+        import parity_util
+    except ImportError:
+        return
+    rec = parity_util.RECORD
+    if not rec:
+        return
+    tol = {"bf16": (parity_util.BF16_MAX_ABS, parity_util.BF16_REL_L2, parity_util.BF16_LSE_ABS),
+           "fp32": (parity_util.F32_MAX_ABS, parity_util.F32_REL_L2, parity_util.F32_LSE_ABS)}
+    tr = terminalreporter
+    tr.section("forward parity margins (achieved / bound)")
+    for dt in ("bf16", "fp32"):
+        rows = [r for r in rec if r[1] == dt]
+        if not rows:
+            continue
+        t = tol[dt]
+        for k, name in ((2, "O max-abs"), (3, "O rel-L2"), (4, "LSE abs")):
+            worst = max(rows, key=lambda r: r[k])
+            tr.write_line(f"{dt} {name}: worst {worst[k]:.3e} (bound {t[k - 2]:.0e}) in "
+                          f"'{worst[0]}' over {len(rows)} checks")

@@ -4,11 +4,14 @@ import numpy as np
 # Output tolerance for bf16 inputs (fp32 accumulation) and for fp32 inputs.
 BF16_MAX_ABS, BF16_REL_L2 = 1e-2, 5e-3
 F32_MAX_ABS, F32_REL_L2 = 1e-5, 1e-5
-# LSE tolerance.  The bf16 kernel sums l over the bf16-rounded probabilities the PV
-# product multiplies; each carries at most 2^-8 relative rounding (round to nearest
-# even, 8 significant bits), so |dLSE| <= ln(1 + 2^-8) = 3.9e-3 plus fp32 terms.
-# The fp32 kernel keeps every quantity in fp32.
-BF16_LSE_ABS, F32_LSE_ABS = 4e-3, 1e-5
+# LSE tolerance (absolute, natural log), as proposed where the task states none: 1e-3 for
+# bf16 inputs, 1e-5 for fp32 inputs.  Both kernels form the row sum from fp32
+# probabilities, so the LSE carries fp32 rounding only.
+BF16_LSE_ABS, F32_LSE_ABS = 1e-3, 1e-5
+
+# Every check() call appends (what, dtype, O max-abs, O rel-L2, LSE abs); conftest prints
+# the worst of them at the end of the session, so the margins show in the test log.
+RECORD = []
 
 
 def dev(x, dtype):
@@ -41,6 +44,7 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
     rel = float(np.linalg.norm(o_gpu - o_ref) / nrm) if nrm > 0 else 0.0
     fin = ~empty
     lse_err = float(np.abs(lse_gpu[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
+    RECORD.append((what, dtype, worst, rel, lse_err))
     assert worst <= max_abs, f"O max-abs {worst:.3e} > {max_abs} {what}"
     assert rel <= rel_l2, f"O rel-L2 {rel:.3e} > {rel_l2} {what}"
     assert lse_err <= lse_tol, f"LSE abs {lse_err:.3e} > {lse_tol} {what}"

@@ -167,3 +167,63 @@ def test_nothing_to_do(gpu_lib):
     o, l = gpu_lib.cpattn_fwd_chunk(q, k, k, [0, 3], [0, 0])     # no keys at all
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+
+
+def test_host_buffers_are_refused_before_any_launch(gpu_lib):
+    """A host tensor given as an output, a gradient or the workspace is refused by the
+    binding (its pointer would be written by a kernel); nothing is launched."""
+    import torch
+    rng = np.random.default_rng(3)
+    q, k, v, cu_q, cu_k, qo, ko = wl.random_pack(rng, 3, 40, 4, 2, 64)
+    Q, K, V = dev(q, "bfloat16"), dev(k, "bfloat16"), dev(v, "bfloat16")
+    tq, hq, d = q.shape
+    host_o = torch.zeros((tq, hq, d), dtype=torch.float32)
+    host_l = torch.zeros((hq, tq), dtype=torch.float32)
+    host_ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="CUDA"):
+        gpu_lib.cpattn_fwd_chunk(Q, K, V, cu_q, cu_k, qo, ko, out=host_o)
+    with pytest.raises(ValueError, match="CUDA"):
+        gpu_lib.cpattn_fwd_chunk(Q, K, V, cu_q, cu_k, qo, ko, lse=host_l)
+    with pytest.raises(ValueError, match="CUDA"):
+        gpu_lib.cpattn_fwd_chunks(Q, [K], [V], cu_q, [cu_k], qo, [ko], workspace=host_ws)
+    o, lse = gpu_lib.cpattn_fwd_chunk(Q, K, V, cu_q, cu_k, qo, ko)
+    do = dev(rng.standard_normal(q.shape).astype(np.float32), "bfloat16")
+    with pytest.raises(ValueError, match="CUDA"):
+        gpu_lib.cpattn_bwd_chunk(Q, K, V, o, lse, do, cu_q, cu_k, qo, ko,
+                                 dk=torch.zeros(k.shape, dtype=torch.float32))
+    with pytest.raises(ValueError, match="CUDA"):
+        gpu_lib.cpattn_bwd_chunks(Q, [K], [V], o, lse, do, cu_q, [cu_k], qo, [ko],
+                                  workspace=host_ws)
+    torch.cuda.synchronize()
+
+
+def test_stream_capture_is_refused(gpu_lib):
+    """A call on a stream that is being captured returns CPATTN_ERR_UNSUPPORTED before
+    anything is enqueued (the plan upload reads a host buffer freed at return)."""
+    import torch
+    rng = np.random.default_rng(4)
+    q, k, v, cu_q, cu_k, qo, ko = wl.random_pack(rng, 2, 50, 4, 2, 64, min_len=1)
+    Q, K, V = dev(q, "bfloat16"), dev(k, "bfloat16"), dev(v, "bfloat16")
+    tq, hq, d = q.shape
+    o = torch.zeros((tq, hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((hq, tq), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    err = None
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        graph.capture_begin()
+        try:
+            gpu_lib.cpattn_fwd_chunk(Q, K, V, cu_q, cu_k, qo, ko, out=o, lse=lse, workspace=ws,
+                                     stream=s)
+        except gpu_lib.CpattnError as e:
+            err = e
+        finally:
+            graph.capture_end()
+    torch.cuda.synchronize()
+    assert err is not None and err.status == 2 and "captur" in str(err)
+    # the library is unaffected: an ordinary call still matches the oracle
+    o2, l2 = gpu_lib.cpattn_fwd_chunk(Q, K, V, cu_q, cu_k, qo, ko)
+    torch.cuda.synchronize()
+    check(host(o2), host(l2), *attention_ref(q, k, v, cu_q, cu_k, qo, ko), "bf16", "after capture")
