@@ -27,7 +27,7 @@ EXPORTED = ("cpattn_workspace_size", "cpattn_workspace_size_chunks", "cpattn_fwd
             "cpattn_bwd_workspace_size", "cpattn_bwd_workspace_size_chunks", "cpattn_merge",
             "cpattn_status_string",
             "cpattn_last_error", "cpattn_plan_build", "cpattn_plan_build_chunks",
-            "cpattn_dcp_schedule")
+            "cpattn_key_plan_build", "cpattn_dcp_schedule")
 MAX_CHUNKS = 16  # CPATTN_MAX_CHUNKS
 
 
@@ -50,6 +50,12 @@ class PlanInfo(ctypes.Structure):
 
 
 PLAN_DTYPE = np.dtype([(name, np.int32) for name, _ in PlanEntry._fields_])
+KEY_TILE_DTYPE = np.dtype([(name, np.int32) for name in
+                           ("row0", "nrows", "q_start", "q_len", "delta", "cost", "chunk", "reserved")])
+
+
+class KeyPlanInfo(ctypes.Structure):
+    _fields_ = [(name, c_int32) for name in ("n_tiles", "keys_per_tile", "query_block", "reserved")]
 
 _lib = None
 _I32P = POINTER(c_int32)
@@ -109,6 +115,10 @@ def load(path: str = LIB_PATH):
     lib.cpattn_plan_build_chunks.argtypes = [_I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
                                              c_int32, c_int32, c_int, c_int32, c_void_p, c_size_t,
                                              POINTER(PlanInfo)]
+    lib.cpattn_key_plan_build.restype = c_int
+    lib.cpattn_key_plan_build.argtypes = [_I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
+                                          c_int32, c_int32, c_int32, c_void_p, c_size_t,
+                                          POINTER(KeyPlanInfo)]
     lib.cpattn_dcp_schedule.restype = c_int
     lib.cpattn_dcp_schedule.argtypes = [_I32P, c_int32, c_int32, c_int32, _I32P, _I32P, _I32P, _I32P,
                                         _I32P]
@@ -208,6 +218,26 @@ def cpattn_plan_build(cu_seqlens_q, cu_seqlens_k, q_pos_offset=None, k_pos_offse
     _check(lib.cpattn_plan_build(pq, pk, pqo, pko, nseq, hq, hkv, d, dtype, int(causal),
                                  c_void_p(entries.ctypes.data), entries.nbytes, ctypes.byref(info)))
     return entries, {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+
+
+def cpattn_key_plan_build(cu_seqlens_q, cu_seqlens_ks: Sequence, q_pos_offset=None,
+                          k_pos_offsets: Optional[Sequence] = None, *, hq: int, hkv: int, d: int,
+                          causal: bool = True):
+    """Host-only key-stationary plan of the backward over the chunks: (tiles, info dict)."""
+    cq, pq = _host_i32(cu_seqlens_q, None, "cu_seqlens_q")
+    nseq = len(cq) - 1
+    qo, pqo = _host_i32(q_pos_offset, nseq, "q_pos_offset")
+    ck, ko = _chunk_meta(cu_seqlens_ks, k_pos_offsets, nseq)
+    lib = load()
+    info = KeyPlanInfo()
+    nch = len(cu_seqlens_ks)
+    _check(lib.cpattn_key_plan_build(pq, _ptr(ck), pqo, _ptr(ko), nch, nseq, hq, hkv, d,
+                                     int(causal), None, 0, ctypes.byref(info)))
+    tiles = np.zeros(info.n_tiles, dtype=KEY_TILE_DTYPE)
+    _check(lib.cpattn_key_plan_build(pq, _ptr(ck), pqo, _ptr(ko), nch, nseq, hq, hkv, d,
+                                     int(causal), c_void_p(tiles.ctypes.data), tiles.nbytes,
+                                     ctypes.byref(info)))
+    return tiles, {name: getattr(info, name) for name, _ in KeyPlanInfo._fields_}
 
 
 def cpattn_dcp_schedule(lengths, world: int, max_seqlen_per_rank: int) -> dict:

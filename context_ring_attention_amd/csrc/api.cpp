@@ -104,6 +104,32 @@ cpattn_status cpattn_plan_build_chunks(const int32_t* cu_seqlens_q, const int32_
   return CPATTN_OK;
 }
 
+cpattn_status cpattn_key_plan_build(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                    int32_t nchunks, int32_t nseq, int32_t hq, int32_t hkv,
+                                    int32_t d, int32_t causal, cpattn_key_tile* plan,
+                                    size_t plan_bytes, cpattn_key_plan_info* info) {
+  clear_error();
+  cpattn_status st = validate_metadata(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset,
+                                       nchunks, nseq, hq, hkv, d);
+  if (st != CPATTN_OK) return st;
+  const int64_t n = count_key_tiles(cu_seqlens_k, nchunks, nseq);
+  if (n > int64_t(INT32_MAX)) return set_error(CPATTN_ERR_UNSUPPORTED, "too many key tiles");
+  const size_t need = size_t(n) * sizeof(cpattn_key_tile);
+  if (plan && plan_bytes < need)
+    return set_error(CPATTN_ERR_WORKSPACE, "plan buffer of %zu bytes, need %zu", plan_bytes, need);
+  if (plan)
+    build_key_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq,
+                      causal, plan, n);
+  if (info) {
+    info->n_tiles = int32_t(n);
+    info->keys_per_tile = kBwdKeysPerTile;
+    info->query_block = kBwdQueryBlock;
+    info->reserved = 0;
+  }
+  return CPATTN_OK;
+}
+
 cpattn_status cpattn_dcp_schedule(const int32_t* lengths, int32_t n, int32_t world,
                                   int32_t max_seqlen_per_rank, int32_t* cp_size,
                                   int32_t* micro_batch, int32_t* group_rank, int32_t* slot,

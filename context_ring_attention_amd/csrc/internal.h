@@ -53,18 +53,9 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdKeysPerTile = 32 * kBwdWaves;
 constexpr int kBwdQueryBlock = 64;
 
-// One tile of the key-stationary plan: kBwdKeysPerTile keys of one sequence in one chunk.
-struct KeyTile {
-  int32_t row0;     // first key row of the tile (in its chunk's K / V)
-  int32_t nrows;    // keys in the tile
-  int32_t q_start;  // first query row of the sequence
-  int32_t q_len;    // queries of the sequence
-  int32_t delta;    // query t (within the sequence) sees tile key r iff t >= delta + r,
-                    // clamped to [-kBwdKeysPerTile, q_len]
-  int32_t cost;     // query blocks to visit, from max(delta, 0) to the last query
-  int32_t chunk;    // chunk of the tile's keys
-  int32_t pad;
-};
+// One tile of the key-stationary plan: kBwdKeysPerTile keys of one sequence in one chunk
+// (the record cpattn_key_plan_build exports).
+using KeyTile = cpattn_key_tile;
 static_assert(sizeof(KeyTile) == 32, "plan records are 32 bytes");
 
 // Number of (chunk, sequence, key block) tiles of the key-stationary plan (cu_k is

@@ -207,7 +207,7 @@ void build_key_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* 
         const int64_t first = std::max<int64_t>(0, delta);
         p.cost = int32_t((nq - first + qb - 1) / qb);
         p.chunk = c;
-        p.pad = 0;
+        p.reserved = 0;
         out[e++] = p;
       }
     }

@@ -319,6 +319,45 @@ cpattn_status cpattn_plan_build_chunks(const int32_t* cu_seqlens_q, const int32_
                                        cpattn_plan_entry* plan, size_t plan_bytes,
                                        cpattn_plan_info* info);
 
+/*
+ * Key-stationary plan of the backward (host only; exposed so the planner can be
+ * checked without a GPU).  The dK/dV kernel processes "key tiles": up to
+ * keys_per_tile consecutive keys of one sequence in one chunk, for one kv head;
+ * it streams, in blocks of query_block queries, the queries of the sequence that
+ * see at least one of the tile's keys.  Tiles are ordered by descending cost
+ * (query blocks to visit), ties in (chunk, sequence, key block) order.
+ */
+typedef struct {
+  int32_t row0;     /* first key row of the tile (index into its chunk's K / V) */
+  int32_t nrows;    /* keys in the tile, 1 .. keys_per_tile */
+  int32_t q_start;  /* first query row of the tile's sequence */
+  int32_t q_len;    /* queries of the sequence */
+  int32_t delta;    /* query t of the sequence sees tile key r iff t >= delta + r
+                       (causal; clamped to [-keys_per_tile, q_len]); -keys_per_tile when not causal */
+  int32_t cost;     /* query blocks from query max(delta, 0) to the sequence's last query */
+  int32_t chunk;    /* chunk of the tile's keys */
+  int32_t reserved;
+} cpattn_key_tile;
+
+typedef struct {
+  int32_t n_tiles;        /* key tiles (work-groups per kv head) */
+  int32_t keys_per_tile;
+  int32_t query_block;    /* queries per inner-loop block */
+  int32_t reserved;
+} cpattn_key_plan_info;
+
+/*
+ * Validate metadata (laid out as for cpattn_bwd_chunks) and build the key plan
+ * cpattn_bwd_chunks would launch.  plan: host buffer of plan_bytes, or NULL to
+ * only fill *info.  Returns CPATTN_ERR_WORKSPACE if plan is non-NULL and
+ * plan_bytes < n_tiles * sizeof(cpattn_key_tile).
+ */
+cpattn_status cpattn_key_plan_build(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                    int32_t nchunks, int32_t nseq, int32_t hq, int32_t hkv,
+                                    int32_t d, int32_t causal, cpattn_key_tile* plan,
+                                    size_t plan_bytes, cpattn_key_plan_info* info);
+
 /* -------------------------------------------------------------------------
  * Dynamic Context Parallelism scheduler (host only, no device work).
  *

@@ -25,18 +25,19 @@ def gpu_lib():
 
 
 def pytest_terminal_summary(terminalreporter):
-    """The achieved forward errors against the oracle, worst first, beside their bounds."""
+    """The worst achieved errors against the oracle (forward and gradients), beside their bounds."""
     try:
         import parity_util
     except ImportError:
         return
     rec = parity_util.RECORD
-    if not rec:
+    grad = parity_util.GRAD_RECORD
+    if not rec and not grad:
         return
     tol = {"bf16": (parity_util.BF16_MAX_ABS, parity_util.BF16_REL_L2, parity_util.BF16_LSE_ABS),
            "fp32": (parity_util.F32_MAX_ABS, parity_util.F32_REL_L2, parity_util.F32_LSE_ABS)}
     tr = terminalreporter
-    tr.section("forward parity margins (achieved / bound)")
+    tr.section("parity margins against the oracle (achieved / bound)")
     for dt in ("bf16", "fp32"):
         rows = [r for r in rec if r[1] == dt]
         if not rows:
@@ -46,3 +47,8 @@ def pytest_terminal_summary(terminalreporter):
             worst = max(rows, key=lambda r: r[k])
             tr.write_line(f"{dt} {name}: worst {worst[k]:.3e} (bound {t[k - 2]:.0e}) in "
                           f"'{worst[0]}' over {len(rows)} checks")
+    if grad:
+        for k, name, bound in ((1, "rel-L2", "5e-03"), (2, "max-abs / max |ref|", "1e-02")):
+            worst = max(grad, key=lambda r: r[k])
+            tr.write_line(f"bf16 gradient {name}: worst {worst[k]:.3e} (bound {bound}) in "
+                          f"'{worst[0]}' over {len(grad)} checks")

@@ -12,6 +12,8 @@ BF16_LSE_ABS, F32_LSE_ABS = 1e-3, 1e-5
 # Every check() call appends (what, dtype, O max-abs, O rel-L2, LSE abs); conftest prints
 # the worst of them at the end of the session, so the margins show in the test log.
 RECORD = []
+# The backward's gradient checks append (what, rel-L2, max-abs / max |ref|).
+GRAD_RECORD = []
 
 
 def dev(x, dtype):

@@ -20,7 +20,7 @@ import pytest
 
 import workloads as wl
 from oracle import attention_bwd_ref, share_bwd_ref
-from parity_util import dev, host
+from parity_util import GRAD_RECORD, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,7 @@ def check_grad(got, ref, what):
         assert worst <= 1e-6, f"{what}: expected zero gradient, max {worst:.3e}"
         return 0.0
     print(f"{what}: rel-L2 {err / nrm:.2e}, max-abs / max {worst / scale:.2e}")
+    GRAD_RECORD.append((what, err / nrm, worst / scale))
     assert err / nrm <= BWD_REL_L2, f"{what}: rel-L2 {err / nrm:.3e} > {BWD_REL_L2}"
     assert worst <= BWD_MAX_REL * scale, f"{what}: max-abs {worst:.3e} > {BWD_MAX_REL} x {scale:.3e}"
     return err / nrm
@@ -134,9 +135,11 @@ def test_backward_accumulates_and_is_deterministic(gpu_lib):
         assert torch.equal(z, x + y)                  # adds into the given buffers
 
 
-def test_backward_cp4_share_full_size_one_group(gpu_lib):
+@pytest.mark.parametrize("kvh", [0, 5])
+def test_backward_cp4_share_full_size(gpu_lib, kvh):
     """The benchmarked share at full size (all heads on the GPU); the oracle differentiates
-    the first GQA group (query heads 0-3, kv head 0)."""
+    one GQA group (query heads 4 kvh .. 4 kvh + 3 and kv head kvh), for the first group and
+    one from the other half of the heads."""
     import torch
     w = wl.make("cp4_share", 0)
     g = w.groups[0]
@@ -148,24 +151,25 @@ def test_backward_cp4_share_full_size_one_group(gpu_lib):
     cus = [c.cu_k for c in g.chunks]
     offs = [c.k_off for c in g.chunks]
     o, lse = gpu_lib.cpattn_fwd_chunks(Q, ks, vs, g.cu_q, cus, g.q_off, offs)
-    sub = wl.Group(q=g.q[:, 0:4], cu_q=g.cu_q, q_off=g.q_off, chunks=[], k_full=g.k_full[:, 0:1],
-                   v_full=g.v_full[:, 0:1], cu_full=g.cu_full)
-    rq, rk, rv = share_bwd_ref(sub, do[:, 0:4])
+    hs = slice(4 * kvh, 4 * kvh + 4)
+    sub = wl.Group(q=g.q[:, hs], cu_q=g.cu_q, q_off=g.q_off, chunks=[],
+                   k_full=g.k_full[:, kvh:kvh + 1], v_full=g.v_full[:, kvh:kvh + 1], cu_full=g.cu_full)
+    rq, rk, rv = share_bwd_ref(sub, do[:, hs])
     lengths = np.diff(g.cu_full)
     # one pass over all chunks, then the ring's order (one call per chunk, dq accumulating)
     for per_chunk in (False, True):
         dq, dks, dvs = gpu_lib.cpattn_share_bwd(Q, ks, vs, o, lse, DO, g.cu_q, cus, g.q_off, offs,
                                                 per_chunk=per_chunk)
         torch.cuda.synchronize()
-        how = "per chunk" if per_chunk else "one pass"
-        check_grad(host(dq)[:, 0:4], rq, f"cp4 dq ({how})")
+        how = f"kv head {kvh}, " + ("per chunk" if per_chunk else "one pass")
+        check_grad(host(dq)[:, hs], rq, f"cp4 dq ({how})")
         # chunk c holds piece c of every sequence: map the oracle's full-sequence key rows
         for c, ch in enumerate(g.chunks):
             rows = np.concatenate([np.arange(g.cu_full[i] + int(ch.k_off[i]),
                                              g.cu_full[i] + int(ch.k_off[i]) + int(ch.cu_k[i + 1] - ch.cu_k[i]))
                                    for i in range(len(lengths))])
-            check_grad(host(dks[c])[:, 0:1], rk[rows], f"cp4 dk chunk {c} ({how})")
-            check_grad(host(dvs[c])[:, 0:1], rv[rows], f"cp4 dv chunk {c} ({how})")
+            check_grad(host(dks[c])[:, kvh:kvh + 1], rk[rows], f"cp4 dk chunk {c} ({how})")
+            check_grad(host(dvs[c])[:, kvh:kvh + 1], rv[rows], f"cp4 dv chunk {c} ({how})")
 
 
 def test_backward_ctx128k_share_full_size(gpu_lib):
@@ -215,7 +219,7 @@ def test_backward_ctx128k_share_full_size(gpu_lib):
     check_grad(dq[tq - m:], rq, "128k dq, last rows")
     check_grad(dk[nk - m:], rk[nk - m:], "128k dk, last keys")
     check_grad(dv[nk - m:], rv[nk - m:], "128k dv, last keys")
-    for t in [0, 1, 127, 128, 16383, int(rng.integers(0, tq - m))]:
+    for t in [0, 1, 127, 128, 16383] + sorted(int(x) for x in rng.integers(0, tq - m, size=27)):
         rq1, _, _ = attention_bwd_ref(g.q[t:t + 1], g.k_full, g.v_full, do[t:t + 1], [0, 1], kk,
                                       [q0 + t], [0], True)
         check_grad(dq[t:t + 1], rq1, f"128k dq row {t}")

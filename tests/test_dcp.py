@@ -161,3 +161,44 @@ def test_library_edges_and_errors():
         with pytest.raises(cra.CpattnError) as e:
             cra.cpattn_dcp_schedule(lengths, world, limit)
         assert e.value.status == cra._binding.ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------------------------
+# hand-derived placements (worked through the reading step by step; see each comment)
+# ---------------------------------------------------------------------------------------------
+def _lib_schedule(lengths, world, limit):
+    r = cra.cpattn_dcp_schedule(lengths, world, limit)
+    return {k: (list(map(int, v)) if k != "n_micro_batches" else v) for k, v in r.items()}
+
+
+def test_world6_mixes_two_rank_and_one_rank_groups_in_one_micro_batch():
+    """world 6, limit 1000, lengths [1900, 1500, 800, 600, 300]:
+    cp sizes: 1900 and 1500 need 2 ranks (950 and 750 per rank), the rest fit one rank.
+    Order 1900, 1500, 800, 600, 300.  1900 opens micro-batch 0 with the pair at rank 0
+    (950 + 950).  1500 does not fit that pair (950 + 750 > 1000), so it opens the pair at
+    rank 2 (750 + 750).  800 finds no one-rank group, and ranks 0-3 are taken, so it opens
+    rank 4.  600 does not fit rank 4 (1400) and opens rank 5.  300 does not fit rank 4
+    (1100) but fits rank 5 (900), as its second sample.  One micro-batch in all."""
+    want = {"cp_size": [2, 2, 1, 1, 1], "micro_batch": [0, 0, 0, 0, 0],
+            "group_rank": [0, 2, 4, 5, 5], "slot": [0, 0, 0, 0, 1], "n_micro_batches": 1}
+    lengths = [1900, 1500, 800, 600, 300]
+    ref = dcp_schedule_ref(lengths, 6, 1000)
+    assert ref == want
+    check_schedule(lengths, 6, 1000, ref)
+    assert _lib_schedule(lengths, 6, 1000) == want
+
+
+def test_a_third_micro_batch_is_opened_when_both_are_full():
+    """world 2, limit 1000, lengths [2000, 1500, 900, 800] (5,200 tokens: at least
+    ceil(5200 / 2000) = 3 micro-batches).  2000 takes the full pair of micro-batch 0
+    (1000 + 1000).  1500 (750 + 750) fits no pair there and the world has one pair, so it
+    opens micro-batch 1.  900 needs one rank, and every rank of micro-batches 0 and 1 is in
+    a pair, so it opens micro-batch 2 at rank 0.  800 does not fit rank 0 there (1700) and
+    opens rank 1 of micro-batch 2."""
+    want = {"cp_size": [2, 2, 1, 1], "micro_batch": [0, 1, 2, 2], "group_rank": [0, 0, 0, 1],
+            "slot": [0, 0, 0, 0], "n_micro_batches": 3}
+    lengths = [2000, 1500, 900, 800]
+    ref = dcp_schedule_ref(lengths, 2, 1000)
+    assert ref == want
+    check_schedule(lengths, 2, 1000, ref)
+    assert _lib_schedule(lengths, 2, 1000) == want

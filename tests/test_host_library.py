@@ -336,3 +336,66 @@ def test_bwd_rejects_bad_arguments_without_a_gpu(lib):
     assert b"overlap" in lib.cpattn_last_error()
     assert cra.cpattn_bwd_workspace_size_chunks(1, [0, 64], [[0, 64]] * 2, 4, 2, 64) >= \
         cra.cpattn_bwd_workspace_size(1, [0, 64], [0, 64], 4, 2, 64)
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 1), (4, 4)])
+def test_key_plan_covers_every_key_once_and_every_query_that_sees_it(hq, hkv):
+    """The backward's key-stationary plan (cpattn_key_plan_build) on random packs split into
+    random chunks: every key row of every chunk is in exactly one tile; a tile's rule
+    (query t sees tile key r iff t >= delta + r) is the causal mask by global position;
+    every query that sees a tile key lies in the visited range [max(delta, 0), q_len), whose
+    length in query blocks is the cost; tiles are ordered longest first."""
+    rng = np.random.default_rng(hq + 3 * hkv)
+    for trial in range(20):
+        causal = trial % 4 != 0
+        nseq = int(rng.integers(0, 5))
+        nch = int(rng.integers(1, 5))
+        lq = rng.integers(0, 300, size=nseq)
+        cu_q = wl.cu_from_lengths(lq)
+        q_off = rng.integers(0, 600, size=nseq).astype(np.int32)
+        cu_ks, k_offs = [], []
+        for c in range(nch):
+            cu_ks.append(wl.cu_from_lengths(rng.integers(0, 400, size=nseq)))
+            k_offs.append(rng.integers(0, 900, size=nseq).astype(np.int32))
+        tiles, info = cra.cpattn_key_plan_build(cu_q, cu_ks, q_off, k_offs, hq=hq, hkv=hkv, d=128,
+                                                causal=causal)
+        kt, qb = info["keys_per_tile"], info["query_block"]
+        assert info["n_tiles"] == len(tiles)
+        cover = [np.zeros(int(ck[-1]), dtype=int) for ck in cu_ks]
+        for t in tiles:
+            c = int(t["chunk"])
+            ck = cu_ks[c]
+            assert 1 <= t["nrows"] <= kt
+            i = int(np.searchsorted(ck, t["row0"], side="right") - 1)
+            assert ck[i] <= t["row0"] and t["row0"] + t["nrows"] <= ck[i + 1]
+            assert (t["row0"] - ck[i]) % kt == 0
+            assert t["q_start"] == cu_q[i] and t["q_len"] == lq[i]
+            cover[c][t["row0"]:t["row0"] + t["nrows"]] += 1
+            nq = int(lq[i])
+            qpos = int(q_off[i]) + np.arange(nq)
+            first = max(int(t["delta"]), 0)
+            for r in range(int(t["nrows"])):
+                kpos = int(k_offs[c][i]) + int(t["row0"] - ck[i]) + r
+                vis = (qpos >= kpos) if causal else np.ones(nq, bool)
+                rule = np.arange(nq) >= int(t["delta"]) + r
+                assert np.array_equal(vis, rule)
+                if vis.any():
+                    assert int(np.nonzero(vis)[0].min()) >= first
+            assert t["cost"] == max(0, -(-(nq - first) // qb))
+        for c in range(nch):
+            assert np.all(cover[c] == 1)
+        costs = tiles["cost"]
+        assert np.all(costs[:-1] >= costs[1:])
+        for a, b in zip(tiles[:-1], tiles[1:]):
+            if a["cost"] == b["cost"]:
+                assert (a["chunk"], a["row0"]) < (b["chunk"], b["row0"])
+
+
+def test_key_plan_rejects_bad_arguments(lib):
+    cu = np.array([0, 10], np.int32)
+    p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    # hq not a multiple of hkv, a bad head dim, a short plan buffer
+    assert lib.cpattn_key_plan_build(p, p, None, None, 1, 1, 6, 4, 128, 1, None, 0, None) == 1
+    assert lib.cpattn_key_plan_build(p, p, None, None, 1, 1, 4, 4, 96, 1, None, 0, None) == 2
+    buf = ctypes.create_string_buffer(16)
+    assert lib.cpattn_key_plan_build(p, p, None, None, 1, 1, 4, 4, 128, 1, buf, 16, None) == 3

@@ -463,3 +463,50 @@ def test_bwd_gqa_equals_summed_mha():
     _close(dq, dq_m, 1e-12)
     _close(dk, dk_m.reshape(dk.shape[0], 2, 3, 8).sum(axis=2), 1e-12)
     _close(dv, dv_m.reshape(dv.shape[0], 2, 3, 8).sum(axis=2), 1e-12)
+
+
+# ----------------------------------------------------------------------------
+# whole-share wrappers: pinned on a multi-sequence CP share with global offsets
+# ----------------------------------------------------------------------------
+from oracle import share_bwd_ref  # noqa: E402
+
+
+@pytest.mark.parametrize("pieces,cp,q_piece,hq,hkv", [([5, 3, 7], 3, 2, 4, 2), ([4, 6], 4, 3, 2, 1),
+                                                      ([9], 2, 0, 3, 3)])
+def test_share_refs_match_sdpa_over_sequences_rebuilt_from_the_chunks(pieces, cp, q_piece, hq, hkv):
+    """share_ref and share_bwd_ref against torch (float64 scaled_dot_product_attention with an
+    explicit mask and its own GQA grouping, autograd for the gradients), per sequence, with
+    the sequence's keys rebuilt from the chunks' pieces and their positions taken from the
+    chunks' offsets: a swapped offset or prefix-sum array in either wrapper changes the
+    result.  The share is one CP rank's (its query piece at q_piece x piece length)."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    rng = np.random.default_rng(31 + cp)
+    d = 8
+    g = wl._even_split_group(rng, pieces, cp, hq, hkv, d, "fp32", q_piece)
+    do = rng.standard_normal(g.q.shape)
+    o_ref, l_ref = share_ref(g)
+    dq_ref, dk_ref, dv_ref = share_bwd_ref(g, do)
+    for i, p in enumerate(pieces):
+        ks = np.concatenate([c.k[c.cu_k[i]:c.cu_k[i + 1]] for c in g.chunks]).astype(np.float64)
+        vs = np.concatenate([c.v[c.cu_k[i]:c.cu_k[i + 1]] for c in g.chunks]).astype(np.float64)
+        kpos = np.concatenate([int(c.k_off[i]) + np.arange(c.cu_k[i + 1] - c.cu_k[i])
+                               for c in g.chunks])
+        assert np.array_equal(kpos, np.arange(cp * p))     # the chunks tile the sequence
+        qpos = q_piece * p + np.arange(p)
+        mask = torch.tensor(kpos[None, :] <= qpos[:, None])
+        Q = torch.tensor(g.q[g.cu_q[i]:g.cu_q[i + 1]].astype(np.float64).transpose(1, 0, 2),
+                         requires_grad=True)
+        K = torch.tensor(ks.transpose(1, 0, 2), requires_grad=True)
+        V = torch.tensor(vs.transpose(1, 0, 2), requires_grad=True)
+        out = F.scaled_dot_product_attention(Q, K, V, attn_mask=mask, enable_gqa=True)
+        scores = (Q @ K.repeat_interleave(hq // hkv, dim=0).transpose(1, 2)) / math.sqrt(d)
+        lse = torch.logsumexp(scores.masked_fill(~mask, -math.inf), dim=-1)
+        rows = slice(int(g.cu_q[i]), int(g.cu_q[i + 1]))
+        np.testing.assert_allclose(o_ref[rows], out.detach().numpy().transpose(1, 0, 2), atol=1e-12)
+        np.testing.assert_allclose(l_ref[:, rows], lse.detach().numpy(), atol=1e-12)
+        (out * torch.tensor(do[rows].transpose(1, 0, 2))).sum().backward()
+        keys = slice(int(g.cu_full[i]), int(g.cu_full[i + 1]))
+        np.testing.assert_allclose(dq_ref[rows], Q.grad.numpy().transpose(1, 0, 2), atol=1e-11)
+        np.testing.assert_allclose(dk_ref[keys], K.grad.numpy().transpose(1, 0, 2), atol=1e-11)
+        np.testing.assert_allclose(dv_ref[keys], V.grad.numpy().transpose(1, 0, 2), atol=1e-11)

@@ -86,9 +86,13 @@ def test_cp4_share_other_packs(gpu_lib, seed):
 
 
 def test_ctx128k_share_full_size(gpu_lib):
+    """The 128K share on a sample of over 4,096 rows x all 8 heads: the first and last row of
+    every 32-token tile (1,024 tiles), every row of the first 128 (the rows that see the
+    fewest keys of the diagonal chunk), and 2,304 random draws (4,242 distinct rows)."""
     w = wl.make("ctx128k_share", 0)
     g = w.groups[0]
-    rows = sample_rows(g.cu_q, 2048, extra=96)
+    rows = np.union1d(sample_rows(g.cu_q, 32, extra=2304, seed=11), np.arange(128))
+    assert len(rows) >= 4096
     _all_modes(gpu_lib, w, g, share_ref(g, rows=rows), rows, "128k share")
 
 
