@@ -33,7 +33,10 @@
 // the swizzle is applied by choosing which global chunk each lane fetches.  Two
 // LDS stages: the next block (of the same chunk, or the first of the next chunk
 // the tile sees) is in flight while the current one is computed; one barrier per
-// block.
+// block.  The tile's blocks are walked as one flat sequence over its chunks, two
+// per loop trip, so the stage of each is a compile-time constant and every LDS
+// read address is a per-lane base plus an immediate offset (no per-block address
+// arithmetic on the VALU, which this kernel is short of).
 //
 // Softmax: scores stay in raw units s = q.k; p = exp2(s * c - m * c) with
 // c = log2(e)/sqrt(D).  The running max m is only moved when a row's block max
@@ -65,6 +68,8 @@
 // are finite or -inf, exp2(-inf) = 0), and without the flag every max over an
 // MFMA result is preceded by a canonicalising v_max_f32 x, x.  Infinities keep
 // their IEEE meaning.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace cpattn {
@@ -86,7 +91,6 @@ struct Layout {
   static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
   static constexpr int kRowBytes = D * 2;
   static constexpr int kTileBytes = BN * kRowBytes;     // one K or V block
-  static constexpr int kStage = 2 * kTileBytes;         // K block then V block
   static constexpr int kRowsPerKB = 1024 / kRowBytes;   // rows one wave-wide load fills
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / kBf16Waves;
 
@@ -102,7 +106,7 @@ struct Layout {
     return row * kRowBytes + ((c ^ k_swz(row)) << 4);
   }
   __device__ static __forceinline__ int v_off(int row, int c) {
-    return kTileBytes + row * kRowBytes + ((c ^ v_swz(row)) << 4);
+    return row * kRowBytes + ((c ^ v_swz(row)) << 4);
   }
 };
 
@@ -142,9 +146,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     float* __restrict__ lse) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = Layout<D>;
-  constexpr int KS = D / 16;  // k-steps of the score MFMA
-  constexpr int DT = D / 32;  // 32-row tiles of O^T
-  __shared__ __attribute__((aligned(1024))) char smem[2 * L::kStage];
+  constexpr int KS = D / 16;      // k-steps of the score MFMA
+  constexpr int DT = D / 32;      // 32-row tiles of O^T
+  constexpr int NPV = 4 * DT;     // PV MFMAs per block: 4 key groups of 16 x DT tiles
+  constexpr int EPS = 32 / NPV;   // softmax elements (per lane) formed beside each PV MFMA
+  // LDS: K stages 0 and 1, then V stages 0 and 1 (one block each).
+  __shared__ __attribute__((aligned(1024))) char smem[4 * L::kTileBytes];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -179,29 +186,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   float l_run = 0.f;        // running sum over this lane's keys
   const float thr = kRescaleLog2 / scale_log2;
 
-  // ---- HBM -> LDS block loads (each wave fills kLoadsPerWave KB of K and of V) ----
-  // Block j of chunk c: rows k_start + 64 j .. of that chunk's K and V.
+  // ---- HBM -> LDS block loads (each wave fills kLoadsPerWave KB of the block) ----
+  // Block j of chunk c: rows k_start + 64 j .. of that chunk's K or V.
   const int64_t stride_bytes = int64_t(hkv) * D * 2;
-  auto issue = [&](int c, int j, int stage) {
+  auto issue = [&](const __bf16* src, int c, int j, char* dst, bool is_v) {
     const cpattn_plan_entry& pc_e = tile[c];
     const int64_t first = (int64_t(pc_e.k_start) + int64_t(j) * BN) * hkv + kvh;
     const int64_t rows_left = int64_t(pc_e.k_len) - int64_t(j) * BN;
-    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kv.k[c] + first * D, rows_left, stride_bytes, D * 2);
-    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(kv.v[c] + first * D, rows_left, stride_bytes, D * 2);
-    char* s = smem + stage * L::kStage;
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(src + first * D, rows_left, stride_bytes, D * 2);
 #pragma unroll
     for (int i = 0; i < L::kLoadsPerWave; ++i) {
       // this wave fills the i-th of its 1 KB pieces; lane l fills bytes [16 l, 16 l + 16)
       const int blk = wave * L::kLoadsPerWave + i;
       const int row = blk * L::kRowsPerKB + lane / L::kChunks;
       const int pc = lane % L::kChunks;                  // physical chunk this lane fills
-      const int voff = row * int(stride_bytes);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(s + blk * 1024), 16,
-                                               voff + ((pc ^ L::k_swz(row)) << 4), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(s + L::kTileBytes + blk * 1024), 16,
-                                               voff + ((pc ^ L::v_swz(row)) << 4), 0, 0, 0);
+      const int swz = is_v ? L::v_swz(row) : L::k_swz(row);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16,
+                                               row * int(stride_bytes) + ((pc ^ swz) << 4), 0, 0, 0);
     }
   };
+  auto kstage = [&](int st) { return smem + st * L::kTileBytes; };
+  auto vstage = [&](int st) { return smem + (2 + st) * L::kTileBytes; };
 
   // Lane-constant parts of the LDS read addresses.
   int k_rd[2][KS];  // S^T A operand: K row 32 kt + n, chunk 2 ks + g
@@ -211,166 +216,169 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int ks = 0; ks < KS; ++ks) k_rd[kt][ks] = L::k_off(32 * kt + n, 2 * ks + g);
   // O^T A operand via transpose reads: lane (n, g) in 16-lane group (g, h = n / 16) supplies the
   // address of V row 16 kk + 4 g + jr (+ 8 for the second half) at columns 32 dt + 16 h + 4 q.
+  // The row swizzle depends only on the row bits that 16 kk and + 8 leave alone, so a lane's
+  // addresses are one base per dt plus immediate offsets.
   const int jr = (n & 15) >> 2, qq = n & 3, hh = n >> 4;
+  int v_rd[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    v_rd[dt] = L::v_off(4 * g + jr, 4 * dt + 2 * hh + (qq >> 1)) + 8 * (qq & 1);
+  // V^T fragment of PV MFMA i (key group i / DT, 32-row tile i % DT) from one V stage.
+  auto vread = [&](const char* vs, int i) {
+    const int kk = i / DT, dt = i % DT;
+    const char* base = vs + v_rd[dt] + 16 * kk * L::kRowBytes;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)base);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * L::kRowBytes));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
 
-  // Chunks the tile sees keys of (cost > 0), in order.
+  // Chunks the tile sees keys of (cost > 0), in order, and the tile's block count.
   auto next_chunk = [&](int c) {
     ++c;
     while (c < nchunks && tile[c].cost == 0) ++c;
     return c;
   };
-
-  int stage = 0;
-  int c = next_chunk(-1);
-  if (c < nchunks) issue(c, 0, 0);
-  for (; c < nchunks;) {
-    const cpattn_plan_entry pe = tile[c];
-    const int cn = next_chunk(c);
-    // This wave's key range in chunk c.
-    int nblk_w = 0, nfull_w = 0;
-    if (rows_w > 0) {
+  int nblk_tile = 0;
+  for (int c = 0; c < nchunks; ++c) nblk_tile += tile[c].cost;
+  // This wave's key blocks in chunk c (a prefix of the tile's) and the unmasked ones among them.
+  auto wave_range = [&](int c, int& nb, int& nf) {
+    nb = 0;
+    nf = 0;
+    if (rows_w > 0 && c < nchunks) {
+      const cpattn_plan_entry pe = tile[c];
       const int kend = max(0, min(pe.k_len, pe.delta + tok0 + rows_w));
-      nblk_w = (kend + BN - 1) / BN;
-      nfull_w = min(min(pe.k_len / BN, max(0, pe.delta + tok0 + 1) / BN), nblk_w);
+      nb = (kend + BN - 1) / BN;
+      nf = min(min(pe.k_len / BN, max(0, pe.delta + tok0 + 1) / BN), nb);
     }
-    const int nblk = pe.cost;  // blocks the whole tile visits in chunk c (uniform)
-    for (int j = 0; j < nblk; ++j, stage ^= 1) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (j + 1 < nblk) issue(c, j + 1, stage ^ 1);
-      else if (cn < nchunks) issue(cn, 0, stage ^ 1);
-      if (j < nblk_w) {
-        const char* s = smem + stage * L::kStage;
-        // ---- S^T = K Q^T for 64 keys (two 32-key tiles) ----
-        // K fragments are read one k-step ahead of the MFMAs that consume them.
-        __builtin_amdgcn_s_setprio(1);
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
-        bf16x8 a0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][0]);
-        bf16x8 a1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][0]);
+  };
+
+  // P = exp2(s c - m c) as bf16 B operands of the PV product (key group kk = registers
+  // 8 (kk % 2) .. +7 of score tile kk / 2) and this lane's sum of the fp32 values.
+  f32x16 s0, s1;
+  bf16x8 pcur[4];
+  auto exp_block = [&](float neg) {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          bf16x8 n0, n1;
-          if (ks + 1 < KS) {
-            n0 = *reinterpret_cast<const bf16x8*>(s + k_rd[0][ks + 1]);
-            n1 = *reinterpret_cast<const bf16x8*>(s + k_rd[1][ks + 1]);
-          }
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
-          if (ks + 1 < KS) {
-            a0 = n0;
-            a1 = n1;
-          }
+    for (int jj = 0; jj < 8; ++jj) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[jj], scale_log2, neg));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[8 + jj], scale_log2, neg));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[jj], scale_log2, neg));
+      const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[8 + jj], scale_log2, neg));
+      pcur[0][jj] = (__bf16)p0;
+      pcur[1][jj] = (__bf16)p1;
+      pcur[2][jj] = (__bf16)p2;
+      pcur[3][jj] = (__bf16)p3;
+      part[0] += p0;
+      part[1] += p1;
+      part[2] += p2;
+      part[3] += p3;
+    }
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  };
+  // ---- the block loop ----
+  // Block p's K and V are staged together; block p + 1's are in flight while p is computed.
+  int lc = next_chunk(-1), lj = 0;  // the next block to load
+  int cc = lc, cj = 0;              // block p
+  int nblk_w = 0, nfull_w = 0;
+  wave_range(cc, nblk_w, nfull_w);
+  if (nblk_tile > 0) {
+    issue(kv.k[lc], lc, lj, kstage(0), false);
+    issue(kv.v[lc], lc, lj, vstage(0), true);
+    if (++lj == tile[lc].cost) lc = next_chunk(lc), lj = 0;
+  }
+  auto step = [&](const int p, auto ST) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (p + 1 < nblk_tile) {
+      issue(kv.k[lc], lc, lj, kstage(1 - ST), false);
+      issue(kv.v[lc], lc, lj, vstage(1 - ST), true);
+      if (++lj == tile[lc].cost) lc = next_chunk(lc), lj = 0;
+    }
+    if (cj < nblk_w) {
+      const char* ks = kstage(ST);
+      const char* vs = vstage(ST);
+      __builtin_amdgcn_s_setprio(1);
+      s0 = f32x16{};
+      s1 = f32x16{};
+      bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ks + k_rd[0][0]);
+      bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ks + k_rd[1][0]);
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        bf16x8 n0, n1;
+        if (k + 1 < KS) {
+          n0 = *reinterpret_cast<const bf16x8*>(ks + k_rd[0][k + 1]);
+          n1 = *reinterpret_cast<const bf16x8*>(ks + k_rd[1][k + 1]);
         }
-        __builtin_amdgcn_s_setprio(0);
-        // ---- mask (diagonal / ragged blocks only) ----
-        if (j >= nfull_w) {
-          // key (within block) of register r: 32 kt + 8 (r / 4) + 4 g + r % 4
-          const int lim = min(pe.k_len - 1, pe.delta + tok0 + n) - j * BN - 4 * g;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kin = 8 * (r >> 2) + (r & 3);
-            if (kin > lim) s0[r] = -INFINITY;
-            if (32 + kin > lim) s1[r] = -INFINITY;
-          }
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[k], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[k], s1, 0, 0, 0);
+        if (k + 1 < KS) {
+          a0 = n0;
+          a1 = n1;
         }
-        // V^T fragments of the first NH key groups, read before the softmax so that their LDS
-        // latency hides behind its VALU work (more groups only add register pressure).
-        constexpr int NH = 1;
-        bf16x8 va[NH][DT];
-#pragma unroll
-        for (int kk = 0; kk < NH; ++kk) {
-          const int row = 16 * kk + 4 * g + jr;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const int c16 = 4 * dt + 2 * hh + (qq >> 1);
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)(s + L::v_off(row, c16) + 8 * (qq & 1)));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)(s + L::v_off(row + 8, c16) + 8 * (qq & 1)));
-            va[kk][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- online softmax ----
-        // P = exp2(s c - m c) as bf16 B operands (key group kk = registers 8 (kk % 2) .. +7 of
-        // tile kk / 2) and this lane's sum of them.
-        bf16x8 pf[4];
-        auto exp_block = [&](float neg) {
-          float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[jj], scale_log2, neg));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[8 + jj], scale_log2, neg));
-            const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[jj], scale_log2, neg));
-            const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[8 + jj], scale_log2, neg));
-            pf[0][jj] = (__bf16)p0;
-            pf[1][jj] = (__bf16)p1;
-            pf[2][jj] = (__bf16)p2;
-            pf[3][jj] = (__bf16)p3;
-            part[0] += p0;
-            part[1] += p1;
-            part[2] += p2;
-            part[3] += p3;
-          }
-          return (part[0] + part[1]) + (part[2] + part[3]);
-        };
-        // Fast path: with a reference max already set, a lane sum <= 2^8 proves every p of the
-        // lane <= 2^8, i.e. no score passed the rescale threshold: the block needs no max.
-        bool slow = __any(m_run == -INFINITY);
-        float lane_sum = 0.f;
-        if (!slow) {
-          lane_sum = exp_block(-m_run * scale_log2);
-          slow = __any(!(lane_sum <= 256.0f));
-        }
-        if (slow) {
-          float mx;
-          {
-            float t[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) t[r] = __builtin_elementwise_max(s0[r], s1[r]);
-#pragma unroll
-            for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-              for (int r = 0; r < w; ++r) t[r] = __builtin_elementwise_max(t[r], t[r + w]);
-            mx = pair_max(t[0]);
-          }
-          if (__any(mx > m_run + thr)) {
-            const float m_new = __builtin_elementwise_max(m_run, mx);
-            const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * scale_log2);
-#pragma unroll
-            for (int i = 0; i < DT; ++i) acc[i] *= alpha;
-            l_run *= alpha;
-            m_run = m_new;
-          }
-          lane_sum = exp_block(-((m_run == -INFINITY) ? 0.f : m_run) * scale_log2);
-        }
-        l_run += lane_sum;
-        // ---- O^T += V^T P^T ----
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int row = 16 * kk + 4 * g + jr;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            bf16x8 a;
-            if (kk < NH) {
-              a = va[kk < NH ? kk : 0][dt];
-            } else {
-              const int c16 = 4 * dt + 2 * hh + (qq >> 1);
-              const int off0 = L::v_off(row, c16) + 8 * (qq & 1);
-              const int off1 = L::v_off(row + 8, c16) + 8 * (qq & 1);
-              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off0));
-              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(s + off1));
-              a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], acc[dt], 0, 0, 0);
-          }
-        }
-        __builtin_amdgcn_s_setprio(0);
       }
+      __builtin_amdgcn_s_setprio(0);
+      if (cj >= nfull_w) {
+        const cpattn_plan_entry pe = tile[cc];
+        const int lim = min(pe.k_len - 1, pe.delta + tok0 + n) - cj * BN - 4 * g;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kin = 8 * (r >> 2) + (r & 3);
+          if (kin > lim) s0[r] = -INFINITY;
+          if (32 + kin > lim) s1[r] = -INFINITY;
+        }
+      }
+      // V^T fragments of the first key group, read before the softmax (LDS latency under VALU).
+      bf16x8 va[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) va[dt] = vread(vs, dt);
+      __builtin_amdgcn_sched_barrier(0);
+      bool slow = __any(m_run == -INFINITY);
+      float lane_sum = 0.f;
+      if (!slow) {
+        lane_sum = exp_block(-m_run * scale_log2);
+        slow = __any(!(lane_sum <= 256.0f));
+      }
+      if (slow) {
+        float mx;
+        {
+          float t[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) t[r] = __builtin_elementwise_max(s0[r], s1[r]);
+#pragma unroll
+          for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int r = 0; r < w; ++r) t[r] = __builtin_elementwise_max(t[r], t[r + w]);
+          mx = pair_max(t[0]);
+        }
+        if (__any(mx > m_run + thr)) {
+          const float m_new = __builtin_elementwise_max(m_run, mx);
+          const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+          const float alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * scale_log2);
+#pragma unroll
+          for (int i = 0; i < DT; ++i) acc[i] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
+        }
+        lane_sum = exp_block(-((m_run == -INFINITY) ? 0.f : m_run) * scale_log2);
+      }
+      l_run += lane_sum;
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const bf16x8 a = i < DT ? va[i] : vread(vs, i);
+        acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pcur[i / DT], acc[i % DT], 0, 0, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
     }
-    c = cn;
+    if (++cj == tile[cc].cost) {
+      cc = next_chunk(cc);
+      cj = 0;
+      wave_range(cc, nblk_w, nfull_w);
+    }
+  };
+  for (int p = 0; p < nblk_tile; p += 2) {
+    step(p, std::integral_constant<int, 0>{});
+    if (p + 1 < nblk_tile) step(p + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = acc / l, LSE = m * scale + ln l (or their merge into o, lse) ----
