@@ -27,7 +27,7 @@ EXPORTED = ("cpattn_workspace_size", "cpattn_workspace_size_chunks", "cpattn_fwd
             "cpattn_bwd_workspace_size", "cpattn_bwd_workspace_size_chunks", "cpattn_merge",
             "cpattn_status_string",
             "cpattn_last_error", "cpattn_plan_build", "cpattn_plan_build_chunks",
-            "cpattn_key_plan_build", "cpattn_dcp_schedule")
+            "cpattn_key_plan_build", "cpattn_dcp_schedule", "cpattn_fwd_chunks_noalloc")
 MAX_CHUNKS = 16  # CPATTN_MAX_CHUNKS
 
 
@@ -84,6 +84,11 @@ def load(path: str = LIB_PATH):
                                       _I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
                                       c_int32, c_int, c_int32, c_int32, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]
+    lib.cpattn_fwd_chunks_noalloc.restype = c_int
+    lib.cpattn_fwd_chunks_noalloc.argtypes = [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int32,
+                                              _I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
+                                              c_int32, c_int, c_int32, c_int32, c_void_p, c_void_p,
+                                              c_void_p]
     lib.cpattn_bwd_chunk.restype = c_int
     lib.cpattn_bwd_chunk.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      _I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
@@ -360,17 +365,9 @@ def cpattn_fwd_chunk_accum(q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos_offset=Non
                     k_pos_offset, causal, out, lse, workspace, stream)
 
 
-def cpattn_fwd_chunks(q, ks: Sequence, vs: Sequence, cu_seqlens_q, cu_seqlens_ks: Sequence,
-                      q_pos_offset=None, k_pos_offsets: Optional[Sequence] = None,
-                      causal: bool = True, accumulate: bool = False, out=None, lse=None,
-                      workspace=None, stream=None) -> Tuple["object", "object"]:
-    """All KV chunks in one launch -> (O, LSE) over the union of their keys.
-
-    ks[c], vs[c]: chunk c's [Tk_c, Hkv, D] CUDA tensors; cu_seqlens_ks[c], k_pos_offsets[c]: its
-    host metadata.  accumulate=True folds the result into the given out/lse.
-    """
-    import torch
-    lib = load()
+def _chunks_args(q, ks, vs, cu_seqlens_q, cu_seqlens_ks, q_pos_offset, k_pos_offsets, accumulate,
+                 out, lse):
+    """Checked host metadata and tensors of a multi-chunk forward call."""
     nch = len(ks)
     if nch != len(vs) or nch != len(cu_seqlens_ks):
         raise ValueError("ks, vs and cu_seqlens_ks must have one entry per chunk")
@@ -405,16 +402,51 @@ def cpattn_fwd_chunks(q, ks: Sequence, vs: Sequence, cu_seqlens_q, cu_seqlens_ks
     if accumulate and (out is None or lse is None):
         raise ValueError("accumulate=True folds into existing out and lse tensors")
     out, lse = _outputs(q, out, lse)
-    need = lib.cpattn_workspace_size_chunks(nseq, pq, hq, hkv, d, nch)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
     kp = (c_void_p * max(nch, 1))(*[t.data_ptr() for t in ks])
     vp = (c_void_p * max(nch, 1))(*[t.data_ptr() for t in vs])
-    _check(lib.cpattn_fwd_chunks(c_void_p(q.data_ptr()), kp, vp, nch, pq, _ptr(ck), pqo, _ptr(ko),
-                                 nseq, hq, hkv, d, dt, int(causal), int(accumulate),
-                                 c_void_p(out.data_ptr()), c_void_p(lse.data_ptr()),
-                                 c_void_p(workspace.data_ptr()), ws_bytes,
-                                 _stream_handle(stream)))
-    return out, lse
+    return dict(nch=nch, nseq=nseq, pq=pq, pqo=pqo, ck=ck, ko=ko, dt=dt, hq=hq, hkv=hkv, d=d,
+                out=out, lse=lse, kp=kp, vp=vp, keep=(cq, qo))
+
+
+def cpattn_fwd_chunks(q, ks: Sequence, vs: Sequence, cu_seqlens_q, cu_seqlens_ks: Sequence,
+                      q_pos_offset=None, k_pos_offsets: Optional[Sequence] = None,
+                      causal: bool = True, accumulate: bool = False, out=None, lse=None,
+                      workspace=None, stream=None) -> Tuple["object", "object"]:
+    """All KV chunks in one launch -> (O, LSE) over the union of their keys.
+
+    ks[c], vs[c]: chunk c's [Tk_c, Hkv, D] CUDA tensors; cu_seqlens_ks[c], k_pos_offsets[c]: its
+    host metadata.  accumulate=True folds the result into the given out/lse.
+    """
+    lib = load()
+    a = _chunks_args(q, ks, vs, cu_seqlens_q, cu_seqlens_ks, q_pos_offset, k_pos_offsets,
+                     accumulate, out, lse)
+    need = lib.cpattn_workspace_size_chunks(a["nseq"], a["pq"], a["hq"], a["hkv"], a["d"], a["nch"])
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    _check(lib.cpattn_fwd_chunks(c_void_p(q.data_ptr()), a["kp"], a["vp"], a["nch"], a["pq"],
+                                 _ptr(a["ck"]), a["pqo"], _ptr(a["ko"]), a["nseq"], a["hq"],
+                                 a["hkv"], a["d"], a["dt"], int(causal), int(accumulate),
+                                 c_void_p(a["out"].data_ptr()), c_void_p(a["lse"].data_ptr()),
+                                 c_void_p(workspace.data_ptr()), ws_bytes, _stream_handle(stream)))
+    return a["out"], a["lse"]
+
+
+def cpattn_fwd_chunks_noalloc(q, ks: Sequence, vs: Sequence, cu_seqlens_q,
+                              cu_seqlens_ks: Sequence, q_pos_offset=None,
+                              k_pos_offsets: Optional[Sequence] = None, causal: bool = True,
+                              accumulate: bool = False, out=None, lse=None,
+                              stream=None) -> Tuple["object", "object"]:
+    """cpattn_fwd_chunks with the work plan in the library's static device scratch (no
+    workspace, no device allocation by the library; pass out and lse to allocate nothing at
+    all).  Calls that overlap on one GPU race on that scratch."""
+    lib = load()
+    a = _chunks_args(q, ks, vs, cu_seqlens_q, cu_seqlens_ks, q_pos_offset, k_pos_offsets,
+                     accumulate, out, lse)
+    _check(lib.cpattn_fwd_chunks_noalloc(c_void_p(q.data_ptr()), a["kp"], a["vp"], a["nch"],
+                                         a["pq"], _ptr(a["ck"]), a["pqo"], _ptr(a["ko"]),
+                                         a["nseq"], a["hq"], a["hkv"], a["d"], a["dt"], int(causal),
+                                         int(accumulate), c_void_p(a["out"].data_ptr()),
+                                         c_void_p(a["lse"].data_ptr()), _stream_handle(stream)))
+    return a["out"], a["lse"]
 
 
 def cpattn_bwd_workspace_size(nseq: int, cu_seqlens_q, cu_seqlens_k, hq: int, hkv: int,

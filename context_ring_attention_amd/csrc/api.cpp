@@ -16,7 +16,7 @@ namespace {
 // state between calls.  The host copy is pageable: the runtime has taken the bytes when
 // hipMemcpyAsync returns, so the buffer can go at once.  A stream being captured into a graph
 // is refused, since a captured copy would re-read that freed host buffer on every replay.
-cpattn_status stage_plan(void* dst, const std::vector<char>& host, hipStream_t stream) {
+cpattn_status stage_plan(void* dst, const char* host, size_t bytes, hipStream_t stream) {
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &cap) != hipSuccess)
     return set_error(CPATTN_ERR_HIP, "hipStreamIsCapturing failed");
@@ -24,9 +24,8 @@ cpattn_status stage_plan(void* dst, const std::vector<char>& host, hipStream_t s
     return set_error(CPATTN_ERR_UNSUPPORTED,
                      "the stream is being captured: the plan upload reads host memory that is "
                      "freed when the call returns");
-  if (host.empty()) return CPATTN_OK;
-  const hipError_t err =
-      hipMemcpyAsync(dst, host.data(), host.size(), hipMemcpyHostToDevice, stream);
+  if (bytes == 0) return CPATTN_OK;
+  const hipError_t err = hipMemcpyAsync(dst, host, bytes, hipMemcpyHostToDevice, stream);
   if (err != hipSuccess)
     return set_error(CPATTN_ERR_HIP, "plan upload failed: %s", hipGetErrorString(err));
   return CPATTN_OK;
@@ -150,15 +149,17 @@ cpattn_status cpattn_plan_build(const int32_t* cu_seqlens_q, const int32_t* cu_s
 
 }  // extern "C"
 
-namespace {
+namespace cpattn {
 
-// Shared body of the three attention entry points.
+// Shared body of the attention entry points.  The plan is built into host_buf (host_cap bytes)
+// when one is given, else into a buffer of its own.
 cpattn_status fwd_impl(const void* q, const void* const* ks, const void* const* vs,
                        int32_t nchunks, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                        const int32_t* q_pos_offset, const int32_t* k_pos_offset, int32_t nseq,
                        int32_t hq, int32_t hkv, int32_t d, cpattn_dtype dtype, int32_t causal,
                        int32_t accumulate, float* o, float* lse, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+                       size_t workspace_bytes, hipStream_t stream, char* host_buf,
+                       size_t host_cap) {
   clear_error();
   if (dtype != CPATTN_BF16 && dtype != CPATTN_FP32)
     return set_error(CPATTN_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
@@ -215,10 +216,17 @@ cpattn_status fwd_impl(const void* q, const void* const* ks, const void* const* 
       return set_error(CPATTN_ERR_INVALID_ARG, "the workspace must not overlap k or v (chunk %d)", c);
   }
 
-  std::vector<char> host(plan_bytes);
+  std::vector<char> own;
+  if (!host_buf) {
+    own.resize(plan_bytes);
+    host_buf = own.data();
+  } else if (host_cap < plan_bytes) {
+    return set_error(CPATTN_ERR_WORKSPACE, "plan of %zu bytes exceeds the %zu-byte staging buffer",
+                     plan_bytes, host_cap);
+  }
   build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal, g,
-                reinterpret_cast<cpattn_plan_entry*>(host.data()), n, nullptr);
-  st = stage_plan(workspace, host, stream);
+                reinterpret_cast<cpattn_plan_entry*>(host_buf), n, nullptr);
+  st = stage_plan(workspace, host_buf, plan_bytes, stream);
   if (st != CPATTN_OK) return st;
   const auto* plan = static_cast<const cpattn_plan_entry*>(workspace);
   hipError_t err;
@@ -244,7 +252,7 @@ cpattn_status fwd_impl(const void* q, const void* const* ks, const void* const* 
   return CPATTN_OK;
 }
 
-}  // namespace
+}  // namespace cpattn
 
 extern "C" {
 
@@ -255,7 +263,7 @@ cpattn_status cpattn_fwd_chunk(const void* q, const void* k, const void* v,
                                cpattn_dtype dtype, int32_t causal, float* o, float* lse,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return fwd_impl(q, &k, &v, 1, cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq, hq,
-                  hkv, d, dtype, causal, 0, o, lse, workspace, workspace_bytes, stream);
+                  hkv, d, dtype, causal, 0, o, lse, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 cpattn_status cpattn_fwd_chunk_accum(const void* q, const void* k, const void* v,
@@ -265,7 +273,7 @@ cpattn_status cpattn_fwd_chunk_accum(const void* q, const void* k, const void* v
                                      cpattn_dtype dtype, int32_t causal, float* o, float* lse,
                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return fwd_impl(q, &k, &v, 1, cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq, hq,
-                  hkv, d, dtype, causal, 1, o, lse, workspace, workspace_bytes, stream);
+                  hkv, d, dtype, causal, 1, o, lse, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void* const* vs,
@@ -276,7 +284,8 @@ cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void
                                 float* o, float* lse, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
   return fwd_impl(q, ks, vs, nchunks, cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nseq,
-                  hq, hkv, d, dtype, causal, accumulate, o, lse, workspace, workspace_bytes, stream);
+                  hq, hkv, d, dtype, causal, accumulate, o, lse, workspace, workspace_bytes, stream,
+                  nullptr, 0);
 }
 
 namespace {
@@ -402,7 +411,7 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
                 reinterpret_cast<cpattn_plan_entry*>(host.data()), n_qt, nullptr);
   build_key_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal,
                     reinterpret_cast<KeyTile*>(host.data() + lay.key_plan_at), lay.n_k);
-  st = stage_plan(ws, host, stream);
+  st = stage_plan(ws, host.data(), host.size(), stream);
   if (st != CPATTN_OK) return st;
   const auto* qplan = reinterpret_cast<const cpattn_plan_entry*>(ws);
   const auto* kplan = reinterpret_cast<const KeyTile*>(ws + lay.key_plan_at);

@@ -76,6 +76,17 @@ struct ChunkPtrs {
 
 cpattn_status set_error(cpattn_status s, const char* fmt, ...);
 
+// Body of the forward entry points (api.cpp): validation, plan, upload into `workspace` on
+// `stream`, launch.  The plan is built into host_buf (host_cap bytes) if one is given, else
+// into a buffer of the call's own.
+cpattn_status fwd_impl(const void* q, const void* const* ks, const void* const* vs,
+                       int32_t nchunks, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       const int32_t* q_pos_offset, const int32_t* k_pos_offset, int32_t nseq,
+                       int32_t hq, int32_t hkv, int32_t d, cpattn_dtype dtype, int32_t causal,
+                       int32_t accumulate, float* o, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, char* host_buf,
+                       size_t host_cap);
+
 // The Dynamic CP scheduler behind cpattn_dcp_schedule (dcp.cpp).
 cpattn_status dcp_schedule(const int32_t* lengths, int32_t n, int32_t world, int32_t limit,
                            int32_t* cp_size, int32_t* micro_batch, int32_t* group_rank,

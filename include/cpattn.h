@@ -165,6 +165,26 @@ cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void
                                 hipStream_t stream);
 
 /*
+ * cpattn_fwd_chunks without a workspace argument, for callers that cannot allocate device
+ * memory (code under graph capture of its own allocations, tight serving loops, harnesses
+ * that forbid hipMalloc): the work plan goes into a static device array of 4 MiB that the
+ * library holds on every GPU it runs on until the process ends (131,072 plan records: e.g.
+ * 4 chunks of a 1M-token query pack in 32-token tiles).  A plan larger than that returns
+ * CPATTN_ERR_UNSUPPORTED with nothing enqueued.  The call allocates nothing, host or device.
+ * All calls on one GPU share that array: calls that overlap on one GPU (different streams,
+ * or threads that do not order their streams) race on it and must not be issued.  The
+ * results equal cpattn_fwd_chunks's for the same arguments.  Other arguments, ownership and
+ * errors as cpattn_fwd_chunks (a stream under capture is refused).
+ */
+cpattn_status cpattn_fwd_chunks_noalloc(const void* q, const void* const* ks,
+                                        const void* const* vs, int32_t nchunks,
+                                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                        const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                        int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
+                                        cpattn_dtype dtype, int32_t causal, int32_t accumulate,
+                                        float* o, float* lse, hipStream_t stream);
+
+/*
  * Backward of one KV chunk: the gradients of the attention the forward computes,
  * i.e. of O = softmax(Q K^T / sqrt(d) + mask) V over all keys of the share, for
  * an upstream gradient dO ("Megatron 6D parallelism guide", section 6: the
