@@ -15,7 +15,7 @@ from ._binding import (  # noqa: F401
     cpattn_bwd_chunks, cpattn_bwd_workspace_size, cpattn_bwd_workspace_size_chunks, cpattn_dcp_schedule,
     cpattn_fwd_chunk,
     cpattn_fwd_chunk_accum, cpattn_fwd_chunks, cpattn_fwd_chunks_noalloc, cpattn_merge,
-    cpattn_plan_build,
+    cpattn_plan_build, cpattn_plan_build_device,
     cpattn_plan_build_chunks, cpattn_key_plan_build, cpattn_workspace_size,
     cpattn_workspace_size_chunks, load,
 )

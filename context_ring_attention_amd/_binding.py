@@ -27,7 +27,8 @@ EXPORTED = ("cpattn_workspace_size", "cpattn_workspace_size_chunks", "cpattn_fwd
             "cpattn_bwd_workspace_size", "cpattn_bwd_workspace_size_chunks", "cpattn_merge",
             "cpattn_status_string",
             "cpattn_last_error", "cpattn_plan_build", "cpattn_plan_build_chunks",
-            "cpattn_key_plan_build", "cpattn_dcp_schedule", "cpattn_fwd_chunks_noalloc")
+            "cpattn_key_plan_build", "cpattn_dcp_schedule", "cpattn_fwd_chunks_noalloc",
+            "cpattn_plan_build_device")
 MAX_CHUNKS = 16  # CPATTN_MAX_CHUNKS
 
 
@@ -124,6 +125,10 @@ def load(path: str = LIB_PATH):
     lib.cpattn_key_plan_build.argtypes = [_I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
                                           c_int32, c_int32, c_int32, c_void_p, c_size_t,
                                           POINTER(KeyPlanInfo)]
+    lib.cpattn_plan_build_device.restype = c_int
+    lib.cpattn_plan_build_device.argtypes = [_I32P, _I32P, _I32P, _I32P, c_int32, c_int32, c_int32,
+                                             c_int32, c_int32, c_int, c_int32, c_void_p, c_size_t,
+                                             c_void_p]
     lib.cpattn_dcp_schedule.restype = c_int
     lib.cpattn_dcp_schedule.argtypes = [_I32P, c_int32, c_int32, c_int32, _I32P, _I32P, _I32P, _I32P,
                                         _I32P]
@@ -205,6 +210,29 @@ def cpattn_plan_build_chunks(cu_seqlens_q, cu_seqlens_ks: Sequence, q_pos_offset
                                         int(causal), c_void_p(entries.ctypes.data), entries.nbytes,
                                         ctypes.byref(info)))
     return entries, {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+
+
+def cpattn_plan_build_device(cu_seqlens_q, cu_seqlens_ks: Sequence, q_pos_offset=None,
+                             k_pos_offsets: Optional[Sequence] = None, *, hq: int, hkv: int, d: int,
+                             dtype: int = BF16, causal: bool = True, stream=None):
+    """The forward's plan built by the device planner, as a numpy array like
+    cpattn_plan_build_chunks's entries (synchronises the stream)."""
+    import torch
+    cq, pq = _host_i32(cu_seqlens_q, None, "cu_seqlens_q")
+    nseq = len(cq) - 1
+    qo, pqo = _host_i32(q_pos_offset, nseq, "q_pos_offset")
+    ck, ko = _chunk_meta(cu_seqlens_ks, k_pos_offsets, nseq)
+    lib = load()
+    nch = len(cu_seqlens_ks)
+    info = PlanInfo()
+    _check(lib.cpattn_plan_build_chunks(pq, _ptr(ck), pqo, _ptr(ko), nch, nseq, hq, hkv, d, dtype,
+                                        int(causal), None, 0, ctypes.byref(info)))
+    buf = torch.zeros(max(info.plan_bytes, 32), dtype=torch.uint8, device="cuda")
+    _check(lib.cpattn_plan_build_device(pq, _ptr(ck), pqo, _ptr(ko), nch, nseq, hq, hkv, d, dtype,
+                                        int(causal), c_void_p(buf.data_ptr()), buf.numel(),
+                                        _stream_handle(stream)))
+    torch.cuda.synchronize()
+    return buf[:info.plan_bytes].cpu().numpy().view(PLAN_DTYPE)
 
 
 def cpattn_plan_build(cu_seqlens_q, cu_seqlens_k, q_pos_offset=None, k_pos_offset=None, *,

@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
 
 SOURCES = ["api.cpp", "plan.cpp", "dcp.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip",
-           "merge.hip", "noalloc.hip"]
+           "merge.hip", "noalloc.hip", "plan_device.hip"]
 # Per-source extra flags.  The bf16 kernels never produce NaN (see their header comments).
 # The forward kernel is scheduled with the backend's iterative ILP strategy, which measured
 # faster than the default occupancy-first one for it.

@@ -129,6 +129,35 @@ cpattn_status cpattn_key_plan_build(const int32_t* cu_seqlens_q, const int32_t* 
   return CPATTN_OK;
 }
 
+cpattn_status cpattn_plan_build_device(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                       const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                       int32_t nchunks, int32_t nseq, int32_t hq, int32_t hkv,
+                                       int32_t d, cpattn_dtype dtype, int32_t causal,
+                                       cpattn_plan_entry* plan, size_t plan_bytes,
+                                       hipStream_t stream) {
+  clear_error();
+  if (dtype != CPATTN_BF16 && dtype != CPATTN_FP32)
+    return set_error(CPATTN_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  cpattn_status st = validate_metadata(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset,
+                                       nchunks, nseq, hq, hkv, d);
+  if (st != CPATTN_OK) return st;
+  const Geometry g = geometry_for(dtype, hq, hkv);
+  const int64_t n = count_tiles(cu_seqlens_q, nseq, g.tokens_per_tile);
+  const size_t need = size_t(n) * nchunks * sizeof(cpattn_plan_entry);
+  if (!plan || plan_bytes < need || !aligned(plan, 16))
+    return set_error(CPATTN_ERR_WORKSPACE, "plan buffer of %zu bytes, need %zu (16-byte aligned)",
+                     plan_bytes, need);
+  PlanMeta meta;
+  if (!fill_plan_meta(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal,
+                      g, n, &meta))
+    return set_error(CPATTN_ERR_UNSUPPORTED, "metadata of %d sequences x %d chunks exceeds the device "
+                     "planner's kernel argument", nseq, nchunks);
+  const hipError_t err = launch_plan_device(meta, plan, stream);
+  if (err != hipSuccess)
+    return set_error(CPATTN_ERR_HIP, "plan kernel launch failed: %s", hipGetErrorString(err));
+  return CPATTN_OK;
+}
+
 cpattn_status cpattn_dcp_schedule(const int32_t* lengths, int32_t n, int32_t world,
                                   int32_t max_seqlen_per_rank, int32_t* cp_size,
                                   int32_t* micro_batch, int32_t* group_rank, int32_t* slot,
@@ -216,20 +245,31 @@ cpattn_status fwd_impl(const void* q, const void* const* ks, const void* const* 
       return set_error(CPATTN_ERR_INVALID_ARG, "the workspace must not overlap k or v (chunk %d)", c);
   }
 
-  std::vector<char> own;
-  if (!host_buf) {
-    own.resize(plan_bytes);
-    host_buf = own.data();
-  } else if (host_cap < plan_bytes) {
-    return set_error(CPATTN_ERR_WORKSPACE, "plan of %zu bytes exceeds the %zu-byte staging buffer",
-                     plan_bytes, host_cap);
-  }
-  build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal, g,
-                reinterpret_cast<cpattn_plan_entry*>(host_buf), n, nullptr);
-  st = stage_plan(workspace, host_buf, plan_bytes, stream);
-  if (st != CPATTN_OK) return st;
-  const auto* plan = static_cast<const cpattn_plan_entry*>(workspace);
+  // The plan: built on the device from the metadata passed by value when it fits the planner's
+  // kernel argument (nothing crosses from host memory at run time, so the call also works under
+  // graph capture), else built here and copied.
+  PlanMeta meta;
   hipError_t err;
+  if (fill_plan_meta(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal,
+                     g, n, &meta)) {
+    err = launch_plan_device(meta, static_cast<cpattn_plan_entry*>(workspace), stream);
+    if (err != hipSuccess)
+      return set_error(CPATTN_ERR_HIP, "plan kernel launch failed: %s", hipGetErrorString(err));
+  } else {
+    std::vector<char> own;
+    if (!host_buf) {
+      own.resize(plan_bytes);
+      host_buf = own.data();
+    } else if (host_cap < plan_bytes) {
+      return set_error(CPATTN_ERR_WORKSPACE, "plan of %zu bytes exceeds the %zu-byte staging buffer",
+                       plan_bytes, host_cap);
+    }
+    build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal, g,
+                  reinterpret_cast<cpattn_plan_entry*>(host_buf), n, nullptr);
+    st = stage_plan(workspace, host_buf, plan_bytes, stream);
+    if (st != CPATTN_OK) return st;
+  }
+  const auto* plan = static_cast<const cpattn_plan_entry*>(workspace);
   if (dtype == CPATTN_BF16) {
     ChunkPtrs<__bf16> kv{};
     for (int32_t c = 0; c < nchunks; ++c) {

@@ -67,6 +67,21 @@ void build_key_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* 
                        const int32_t* k_off, int32_t nchunks, int32_t nseq, int32_t causal,
                        KeyTile* out, int64_t n_tiles);
 
+// Metadata of a forward call passed by value to the device planner: cu_q [nseq + 1], q_off
+// [nseq], then per chunk cu_k [nseq + 1] and k_off [nseq].  Calls whose metadata does not fit
+// build their plan on the host and copy it instead.
+constexpr int kPlanMetaInts = 480;
+struct PlanMeta {
+  int32_t nseq, nchunks, causal, tt, bn, n_tiles;
+  int32_t v[kPlanMetaInts];
+};
+// Fill m for these arguments; false if they do not fit (or nseq == 0).
+bool fill_plan_meta(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_off,
+                    const int32_t* k_off, int32_t nchunks, int32_t nseq, int32_t causal,
+                    const Geometry& g, int64_t n_tiles, PlanMeta* m);
+// Writes build_entries' plan (n_tiles * nchunks entries) into device memory `out` on `stream`.
+hipError_t launch_plan_device(const PlanMeta& m, cpattn_plan_entry* out, hipStream_t stream);
+
 // Device pointers of the chunks of one launch (passed by value as a kernel argument).
 template <class T>
 struct ChunkPtrs {

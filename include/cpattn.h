@@ -65,14 +65,15 @@ typedef enum {
  * the arguments are invalid (nseq < 0, null cu_seqlens_q with nseq > 0, hq or
  * hkv < 1).
  *
- * Work plans: every call builds its plan on the host and copies it into the
- * first bytes of the caller's workspace on `stream`, ahead of the kernels that
- * read it.  The library allocates nothing and keeps no state between calls;
- * consecutive calls on one stream may reuse one workspace (stream order keeps a
- * plan until its kernels have run).  Calls on different streams need different
- * workspaces.  A stream that is being captured into a graph is refused
- * (CPATTN_ERR_UNSUPPORTED): the upload reads a host buffer that is freed when the
- * call returns.
+ * Work plans: every call writes its plan into the first bytes of the caller's workspace on
+ * `stream`, ahead of the kernels that read it.  When the call's metadata is small (see
+ * cpattn_plan_build_device) a planner kernel builds it on the device from the metadata passed
+ * by value; otherwise it is built on the host and copied.  The library allocates no device
+ * memory and keeps no state between calls; consecutive calls on one stream may reuse one
+ * workspace (stream order keeps a plan until its kernels have run).  Calls on different
+ * streams need different workspaces.  A stream that is being captured into a graph is refused
+ * (CPATTN_ERR_UNSUPPORTED) when the plan would be copied from host memory (that host buffer is
+ * freed when the call returns); device-planned calls may be captured.
  */
 size_t cpattn_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q, int32_t hq, int32_t hkv,
                              int32_t d);
@@ -107,7 +108,9 @@ size_t cpattn_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_q, i
  *                    above); it must not overlap q, k, v, o or lse.
  * The caller owns every buffer; o must not overlap q, k or v.  Rows of o/lse for
  * queries of zero-length key sequences are written as (0, -inf).
- * Returns CPATTN_OK, or an error code with nothing enqueued.
+ * Returns CPATTN_OK, or an error code: invalid arguments (every code but CPATTN_ERR_HIP)
+ * return before anything is enqueued; a failed launch (CPATTN_ERR_HIP) may leave the plan's
+ * upload or planner kernel enqueued.
  */
 cpattn_status cpattn_fwd_chunk(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -154,7 +157,7 @@ cpattn_status cpattn_fwd_chunk_accum(const void* q, const void* k, const void* v
  *   o, lse       device [Tq, hq, d] / [hq, Tq] fp32 (written; read too if accumulate)
  *   workspace    device, >= cpattn_workspace_size_chunks(..., nchunks) bytes, 256-byte aligned
  * The chunks may differ in length per sequence (zero allowed).  o must not
- * overlap q or any chunk.  Returns CPATTN_OK, or an error code with nothing enqueued.
+ * overlap q or any chunk.  Returns and errors as cpattn_fwd_chunk.
  */
 cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void* const* vs,
                                 int32_t nchunks, const int32_t* cu_seqlens_q,
@@ -377,6 +380,22 @@ cpattn_status cpattn_key_plan_build(const int32_t* cu_seqlens_q, const int32_t* 
                                     int32_t nchunks, int32_t nseq, int32_t hq, int32_t hkv,
                                     int32_t d, int32_t causal, cpattn_key_tile* plan,
                                     size_t plan_bytes, cpattn_key_plan_info* info);
+
+/*
+ * The same plan as cpattn_plan_build_chunks, built on the device into `plan` (device, at least
+ * the plan's bytes, 16-byte aligned) on `stream` from the metadata passed by value.  This is
+ * how the forward entry points build their plan when the metadata is small enough:
+ * (2 nseq + 1) (nchunks + 1) <= 480 int32 values, e.g. up to 47 sequences at 4 chunks or 119
+ * sequences in one chunk; larger metadata is planned on the host and copied.  Returns
+ * CPATTN_ERR_UNSUPPORTED for metadata that does not fit (or nseq == 0).  Exposed so the two
+ * planners can be compared.
+ */
+cpattn_status cpattn_plan_build_device(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                       const int32_t* q_pos_offset, const int32_t* k_pos_offset,
+                                       int32_t nchunks, int32_t nseq, int32_t hq, int32_t hkv,
+                                       int32_t d, cpattn_dtype dtype, int32_t causal,
+                                       cpattn_plan_entry* plan, size_t plan_bytes,
+                                       hipStream_t stream);
 
 /* -------------------------------------------------------------------------
  * Dynamic Context Parallelism scheduler (host only, no device work).

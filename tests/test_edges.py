@@ -197,12 +197,13 @@ def test_host_buffers_are_refused_before_any_launch(gpu_lib):
     torch.cuda.synchronize()
 
 
-def test_stream_capture_is_refused(gpu_lib):
-    """A call on a stream that is being captured returns CPATTN_ERR_UNSUPPORTED before
-    anything is enqueued (the plan upload reads a host buffer freed at return)."""
+def test_stream_capture_is_refused_for_host_planned_calls(gpu_lib):
+    """A call whose plan is built on the host and copied (metadata too large for the device
+    planner: here 300 sequences) returns CPATTN_ERR_UNSUPPORTED on a stream that is being
+    captured, before anything is enqueued (the copy would read a host buffer freed at return)."""
     import torch
     rng = np.random.default_rng(4)
-    q, k, v, cu_q, cu_k, qo, ko = wl.random_pack(rng, 2, 50, 4, 2, 64, min_len=1)
+    q, k, v, cu_q, cu_k, qo, ko = wl.random_pack(rng, 300, 6, 4, 2, 64, min_len=1)
     Q, K, V = dev(q, "bfloat16"), dev(k, "bfloat16"), dev(v, "bfloat16")
     tq, hq, d = q.shape
     o = torch.zeros((tq, hq, d), dtype=torch.float32, device="cuda")
@@ -227,3 +228,31 @@ def test_stream_capture_is_refused(gpu_lib):
     o2, l2 = gpu_lib.cpattn_fwd_chunk(Q, K, V, cu_q, cu_k, qo, ko)
     torch.cuda.synchronize()
     check(host(o2), host(l2), *attention_ref(q, k, v, cu_q, cu_k, qo, ko), "bf16", "after capture")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_many_sequences_host_planned(gpu_lib, dtype):
+    """200 short sequences in 3 chunks: metadata too large for the device planner, so the plan
+    is built on the host and copied; all rows against the oracle."""
+    rng = np.random.default_rng(17)
+    q, k, v, cu_q, cu_k, qo, ko = wl.random_pack(rng, 200, 12, 4, 2, 64, dtype=dtype, min_len=1)
+    dt = "bfloat16" if dtype == "bf16" else "float32"
+    Q, K, V = dev(q, dt), dev(k, dt), dev(v, dt)
+    # three chunks: cut every sequence's keys at two points
+    cuts = [sorted(rng.integers(0, cu_k[i + 1] - cu_k[i] + 1, size=2).tolist()) for i in range(200)]
+    ks, vs, cus, offs = [], [], [], []
+    for c in range(3):
+        rows, lens, off = [], [], []
+        for i in range(200):
+            b = [0] + cuts[i] + [int(cu_k[i + 1] - cu_k[i])]
+            rows.append(np.arange(cu_k[i] + b[c], cu_k[i] + b[c + 1]))
+            lens.append(b[c + 1] - b[c])
+            off.append(int(ko[i]) + b[c])
+        r = np.concatenate(rows).astype(np.int64)
+        ks.append(K[r].contiguous()); vs.append(V[r].contiguous())
+        cus.append(wl.cu_from_lengths(lens)); offs.append(np.array(off, np.int32))
+    o, lse = gpu_lib.cpattn_fwd_chunks(Q, ks, vs, cu_q, cus, qo, offs)
+    import torch
+    torch.cuda.synchronize()
+    check(host(o), host(lse), *attention_ref(q, k, v, cu_q, cu_k, qo, ko), dtype,
+          f"200 sequences, host-planned ({dtype})")

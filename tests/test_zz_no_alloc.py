@@ -1,7 +1,7 @@
 """cpattn_fwd_chunks_noalloc (plan in the library's static device scratch) against
 cpattn_fwd_chunks (plan in a caller workspace), through the C ABI.
 
-Two calls in a row on one stream, the second with a smaller input, each compared with the
+Calls in a row on one stream, the second with a smaller input, each compared with the
 workspace entry point's output on the same inputs (bit for bit: same kernels, same plan) and
 with the oracle to the parity bar; a plan beyond the static scratch is refused.
 """
@@ -37,10 +37,14 @@ def test_noalloc_equals_workspace_entry_point_on_two_calls(gpu_lib):
     big = wl.make("cp4_share", 0).groups[0]
     rng = np.random.default_rng(42)
     small = wl._even_split_group(rng, [300, 77, 5], 2, 32, 8, 128, "bf16", 1)
-    for name, g in (("cp4 share", big), ("small share", small)):
+    # third: 150 short sequences (metadata too large for the device planner: the plan is built
+    # in the entry point's static host buffer and copied into the static device scratch)
+    many = wl._even_split_group(rng, [int(x) for x in rng.integers(1, 20, size=150)], 2, 4, 2, 64,
+                                "bf16", 1)
+    for name, g in (("cp4 share", big), ("small share", small), ("many sequences", many)):
         o_ws, l_ws, o_na, l_na = _run_both(gpu_lib, g, "bfloat16")
         assert torch.equal(o_na, o_ws) and torch.equal(l_na, l_ws), name
-        rows = np.arange(int(g.cu_q[-1])) if name == "small share" else \
+        rows = np.arange(int(g.cu_q[-1])) if name != "cp4 share" else \
             np.unique(np.linspace(0, int(g.cu_q[-1]) - 1, 300).astype(np.int64))
         check(host(o_na)[rows], host(l_na)[:, rows], *share_ref(g, rows=rows), "bf16",
               f"no-alloc {name}")
