@@ -45,15 +45,17 @@
 // O / l cancels the common factor exactly.  This skips the 64-register rescale
 // of the accumulator on almost every block.
 //
-// Row sums are taken over the fp32 probabilities, before they are rounded to
-// bf16 for the PV product, so the LSE carries only fp32 rounding (a sum over
-// the rounded values would be off by up to 2^-9 of each term, which for rows
-// with few visible keys moves the LSE by more than 1e-3).  Most blocks skip the
-// row max altogether: once a reference max is set, P is formed against it
-// directly, and a lane sum <= 2^8 proves no score passed the threshold (every
-// p >= 0), which is all the max was needed for; otherwise the block is redone
-// with the max (and rescale) first.  Both paths give the same bits as always
-// taking the max.
+// Two row sums are kept: over the fp32 probabilities (for the LSE, which then
+// carries fp32 rounding only; a sum over bf16-rounded values would be off by up
+// to 2^-9 of each term, which moves the LSE of rows with few keys by more than
+// 1e-3), and over their bf16 roundings with v_dot2_f32_bf16 (for O, which is then
+// an exact convex combination of the weights the PV product multiplied; dividing
+// by the fp32 sum instead would scale O by the rounding of the largest weight,
+// which under the lazy max below need not be 1).  Most blocks skip the row max
+// altogether: once a reference max is set, P is formed against it directly, and a
+// lane sum <= 2^8 proves no score passed the threshold (every p >= 0), which is
+// all the max was needed for; otherwise the block is redone with the max (and
+// rescale) first.  Both paths give the same bits as always taking the max.
 //
 // Scheduling: the two waves of a SIMD (one from each of the CU's two
 // work-groups) run the same block loop; a wave raises its issue priority for
@@ -77,6 +79,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -183,7 +186,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
   float m_run = -INFINITY;  // running reference max of raw scores (row n)
-  float l_run = 0.f;        // running sum over this lane's keys
+  float l_run = 0.f;        // running sum of this lane's fp32 weights (for the LSE)
+  float lb_run = 0.f;       // running sum of the same weights rounded to bf16 (for O)
   const float thr = kRescaleLog2 / scale_log2;
 
   // ---- HBM -> LDS block loads (each wave fills kLoadsPerWave KB of the block) ----
@@ -256,6 +260,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   // 8 (kk % 2) .. +7 of score tile kk / 2) and this lane's sum of the fp32 values.
   f32x16 s0, s1;
   bf16x8 pcur[4];
+  struct Sums {
+    float p, b;  // the lane's sum of the fp32 weights and of their bf16 roundings
+  };
   auto exp_block = [&](float neg) {
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -273,7 +280,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       part[2] += p2;
       part[3] += p3;
     }
-    return (part[0] + part[1]) + (part[2] + part[3]);
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float pb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      pb[kk] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pb[kk] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pcur[kk][2 * i], pcur[kk][2 * i + 1]}, ones,
+                                                 pb[kk], false);
+    }
+    return Sums{(part[0] + part[1]) + (part[2] + part[3]), (pb[0] + pb[1]) + (pb[2] + pb[3])};
   };
   // ---- the block loop ----
   // Block p's K and V are staged together; block p + 1's are in flight while p is computed.
@@ -333,10 +350,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       for (int dt = 0; dt < DT; ++dt) va[dt] = vread(vs, dt);
       __builtin_amdgcn_sched_barrier(0);
       bool slow = __any(m_run == -INFINITY);
-      float lane_sum = 0.f;
+      Sums lane_sum = {0.f, 0.f};
       if (!slow) {
         lane_sum = exp_block(-m_run * scale_log2);
-        slow = __any(!(lane_sum <= 256.0f));
+        slow = __any(!(lane_sum.p <= 256.0f));
       }
       if (slow) {
         float mx;
@@ -357,11 +374,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
           for (int i = 0; i < DT; ++i) acc[i] *= alpha;
           l_run *= alpha;
+          lb_run *= alpha;
           m_run = m_new;
         }
         lane_sum = exp_block(-((m_run == -INFINITY) ? 0.f : m_run) * scale_log2);
       }
-      l_run += lane_sum;
+      l_run += lane_sum.p;
+      lb_run += lane_sum.b;
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
@@ -381,14 +400,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     if (p + 1 < nblk_tile) step(p + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- epilogue: O = acc / l, LSE = m * scale + ln l (or their merge into o, lse) ----
+  // ---- epilogue: O = acc / l_b, LSE = m * scale + ln l (or their merge into o, lse) ----
+  // O is divided by the sum of the bf16 weights the PV product multiplied (an exact convex
+  // combination of the values, whatever the rounding of the largest weight under the lazy
+  // max), the LSE is taken from the sum of the fp32 weights.
   const float l_tot = pair_sum(l_run);
+  const float lb_tot = pair_sum(lb_run);
   if (n < rows_w) {
     const int64_t row = row0 + tok0 + n;
     float* op = o + (row * hq + head) * D + 4 * g;
     float* lp = lse + int64_t(head) * tq_total + row;
     const float lse_new = l_tot > 0.f ? m_run * scale + logf(l_tot) : -INFINITY;
-    float wa = 0.f, wb = l_tot > 0.f ? 1.0f / l_tot : 0.f, lse_out = lse_new;
+    float wa = 0.f, wb = l_tot > 0.f ? 1.0f / lb_tot : 0.f, lse_out = lse_new;
     bool write = true;
     if (ACCUM) {
       // (O, LSE) <- merge((O, LSE), (acc / l, lse_new)); an empty side leaves the other exact.
@@ -400,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         const float ea = expf(lse_old - mm), eb = expf(lse_new - mm);
         const float inv = 1.0f / (ea + eb);
         wa = ea * inv;
-        wb = eb * inv / l_tot;
+        wb = eb * inv / lb_tot;
         lse_out = mm + logf(ea + eb);
       }
     }
