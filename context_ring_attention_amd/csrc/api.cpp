@@ -150,8 +150,8 @@ cpattn_status cpattn_plan_build_device(const int32_t* cu_seqlens_q, const int32_
   PlanMeta meta;
   if (!fill_plan_meta(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal,
                       g, n, &meta))
-    return set_error(CPATTN_ERR_UNSUPPORTED, "metadata of %d sequences x %d chunks exceeds the device "
-                     "planner's kernel argument", nseq, nchunks);
+    return set_error(CPATTN_ERR_UNSUPPORTED, "%d sequences x %d chunks (%lld token tiles) exceed the "
+                     "device planner's limits", nseq, nchunks, (long long)n);
   const hipError_t err = launch_plan_device(meta, plan, stream);
   if (err != hipSuccess)
     return set_error(CPATTN_ERR_HIP, "plan kernel launch failed: %s", hipGetErrorString(err));

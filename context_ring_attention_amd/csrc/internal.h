@@ -68,14 +68,16 @@ void build_key_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* 
                        KeyTile* out, int64_t n_tiles);
 
 // Metadata of a forward call passed by value to the device planner: cu_q [nseq + 1], q_off
-// [nseq], then per chunk cu_k [nseq + 1] and k_off [nseq].  Calls whose metadata does not fit
-// build their plan on the host and copy it instead.
+// [nseq], then per chunk cu_k [nseq + 1] and k_off [nseq].  Calls whose metadata does not fit,
+// or whose plan has more than kPlanDeviceMaxTiles token tiles, build their plan on the host and
+// copy it instead.
 constexpr int kPlanMetaInts = 480;
+constexpr int kPlanDeviceMaxTiles = 4096;
 struct PlanMeta {
   int32_t nseq, nchunks, causal, tt, bn, n_tiles;
   int32_t v[kPlanMetaInts];
 };
-// Fill m for these arguments; false if they do not fit (or nseq == 0).
+// Fill m for these arguments; false if they do not fit (or nseq == 0, or n_tiles is too large).
 bool fill_plan_meta(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_off,
                     const int32_t* k_off, int32_t nchunks, int32_t nseq, int32_t causal,
                     const Geometry& g, int64_t n_tiles, PlanMeta* m);

@@ -3,80 +3,118 @@
 //
 // The plan is the one build_entries (plan.cpp) writes: one entry per (sequence, token tile) and
 // chunk, tiles ordered by their total cost over the chunks, longest first, ties in (sequence,
-// tile) order.  Here every thread owns one tile: it finds its sequence and tile from the
-// per-sequence tile counts, forms its entries, and computes its position in that order by
-// counting the tiles that precede it.  Within one sequence a tile's cost never decreases with
-// its index (each chunk's visible key range only grows, and the ragged last tile ends at the
-// sequence's last query), so the count over each sequence is two binary searches.
+// tile) order.  One work-group of 1024 threads builds it: the metadata goes to LDS, every
+// thread forms the total of some tiles and packs it with the tile's index into one 64-bit key
+// (INT32_MAX - total above the index, so ascending keys are the plan's order), a bitonic sort
+// in LDS orders the keys, and each thread then writes the entries of some positions of the
+// sorted order.  Every step reads LDS only, so the kernel takes a few microseconds for the
+// plans it accepts (at most kPlanDeviceMaxTiles tiles).
 #include "internal.h"
 
 namespace cpattn {
 namespace {
 
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMaxSeq = (kPlanMetaInts / 2 - 1) / 2;   // (2 nseq + 1) * 2 <= kPlanMetaInts
+
+// Metadata accessors over the LDS copy of PlanMeta::v.  Tile and block sizes are powers of two
+// (their logarithms tt_log, bn_log), so the divisions are shifts.
 struct Meta {
-  const PlanMeta& m;
-  __device__ int cu_q(int i) const { return m.v[i]; }
-  __device__ int q_off(int i) const { return m.v[m.nseq + 1 + i]; }
-  __device__ const int32_t* chunk(int c) const { return m.v + (2 * m.nseq + 1) * (c + 1); }
+  const int32_t* v;
+  int nseq, nchunks, causal, tt, bn, tt_log, bn_log;
+  __device__ int cu_q(int i) const { return v[i]; }
+  __device__ int q_off(int i) const { return v[nseq + 1 + i]; }
+  __device__ const int32_t* chunk(int c) const { return v + (2 * nseq + 1) * (c + 1); }
   __device__ int cu_k(int c, int i) const { return chunk(c)[i]; }
-  __device__ int k_off(int c, int i) const { return chunk(c)[m.nseq + 1 + i]; }
-  __device__ int tiles(int i) const { return (cu_q(i + 1) - cu_q(i) + m.tt - 1) / m.tt; }
+  __device__ int k_off(int c, int i) const { return chunk(c)[nseq + 1 + i]; }
+  __device__ int tiles(int i) const { return int((int64_t(cu_q(i + 1) - cu_q(i)) + tt - 1) >> tt_log); }
 
   // Entry of sequence i, tile tb, chunk c (as build_entries forms it).
   __device__ cpattn_plan_entry entry(int i, int tb, int c) const {
     const int nq = cu_q(i + 1) - cu_q(i);
     const int nk = cu_k(c, i + 1) - cu_k(c, i);
     cpattn_plan_entry p;
-    p.row0 = cu_q(i) + tb * m.tt;
-    p.nrows = min(m.tt, nq - tb * m.tt);
+    p.row0 = cu_q(i) + tb * tt;
+    p.nrows = min(tt, nq - tb * tt);
     p.k_start = cu_k(c, i);
     p.k_len = nk;
-    int64_t delta = m.causal ? (int64_t(q_off(i)) + int64_t(tb) * m.tt - k_off(c, i)) : int64_t(nk);
-    delta = max(int64_t(-m.tt), min(delta, int64_t(nk)));
+    int64_t delta = causal ? (int64_t(q_off(i)) + int64_t(tb) * tt - k_off(c, i)) : int64_t(nk);
+    delta = max(int64_t(-tt), min(delta, int64_t(nk)));
     p.delta = int32_t(delta);
     const int64_t kend = max(int64_t(0), min(int64_t(nk), delta + p.nrows));
-    p.cost = int32_t((kend + m.bn - 1) / m.bn);
+    p.cost = int32_t((kend + bn - 1) >> bn_log);
     p.seq = i;
     p.tblock = tb;
     return p;
   }
-  __device__ int64_t total(int i, int tb) const {
-    int64_t s = 0;
-    for (int c = 0; c < m.nchunks; ++c) s += entry(i, tb, c).cost;
-    return s;
-  }
-  // Number of tiles of sequence i whose total is < x (strict) or <= x.
-  __device__ int count_below(int i, int64_t x, bool inclusive) const {
-    int lo = 0, hi = tiles(i);
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      const int64_t t = total(i, mid);
-      if (inclusive ? (t <= x) : (t < x)) lo = mid + 1;
-      else hi = mid;
-    }
-    return lo;
-  }
 };
 
-__global__ __launch_bounds__(256) void plan_kernel(const PlanMeta meta, cpattn_plan_entry* out) {
-  const Meta M{meta};
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= meta.n_tiles) return;
-  // sequence and tile of global tile t
-  int i = 0, first = 0;
-  while (first + M.tiles(i) <= t) first += M.tiles(i++);
-  const int tb = t - first;
-  const int64_t mine = M.total(i, tb);
-  // tiles before t in the longest-first order: every tile with a larger total, and the
-  // earlier tiles (in sequence, tile order) with the same total
-  int64_t rank = 0;
-  for (int j = 0; j < meta.nseq; ++j) {
-    const int le = M.count_below(j, mine, true);
-    rank += M.tiles(j) - le;
-    if (j < i) rank += le - M.count_below(j, mine, false);
-    else if (j == i) rank += tb - M.count_below(j, mine, false);
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const PlanMeta meta,
+                                                            cpattn_plan_entry* out) {
+  __shared__ int32_t sv[kPlanMetaInts];
+  __shared__ int32_t first[kPlanMaxSeq + 1];   // first tile of each sequence, then n_tiles
+  __shared__ uint64_t key[kPlanDeviceMaxTiles];
+  const int tid = threadIdx.x;
+  const int nseq = meta.nseq, nch = meta.nchunks, n = meta.n_tiles;
+  const int used = (2 * nseq + 1) * (nch + 1);
+  for (int i = tid; i < used; i += kPlanThreads) sv[i] = meta.v[i];
+  __syncthreads();
+  const Meta M{sv, nseq, nch, meta.causal, meta.tt, meta.bn, __builtin_ctz(unsigned(meta.tt)),
+               __builtin_ctz(unsigned(meta.bn))};
+  if (tid == 0) {
+    int acc = 0;
+    for (int i = 0; i < nseq; ++i) {
+      first[i] = acc;
+      acc += M.tiles(i);
+    }
+    first[nseq] = acc;
   }
-  for (int c = 0; c < meta.nchunks; ++c) out[rank * meta.nchunks + c] = M.entry(i, tb, c);
+  __syncthreads();
+  // sequence of tile t: the last i with first[i] <= t (empty sequences share their first)
+  auto seq_of = [&](int t) {
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+
+  int N = 1;
+  while (N < n) N <<= 1;
+  for (int t = tid; t < N; t += kPlanThreads) {
+    uint64_t k = ~uint64_t(0);   // padding sorts last
+    if (t < n) {
+      const int i = seq_of(t), tb = t - first[i];
+      int32_t total = 0;
+      for (int c = 0; c < nch; ++c) total += M.entry(i, tb, c).cost;
+      k = (uint64_t(uint32_t(INT32_MAX - total)) << 32) | uint32_t(t);
+    }
+    key[t] = k;
+  }
+  __syncthreads();
+  // bitonic sort of key[0, N), ascending
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < N; i += kPlanThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint64_t a = key[i], b = key[l];
+          if ((a > b) == ((i & k) == 0)) {
+            key[i] = b;
+            key[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = tid; r < n; r += kPlanThreads) {
+    const int t = int(uint32_t(key[r]));
+    const int i = seq_of(t), tb = t - first[i];
+    for (int c = 0; c < nch; ++c) out[int64_t(r) * nch + c] = M.entry(i, tb, c);
+  }
 }
 
 }  // namespace
@@ -85,7 +123,10 @@ bool fill_plan_meta(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_o
                     const int32_t* k_off, int32_t nchunks, int32_t nseq, int32_t causal,
                     const Geometry& g, int64_t n_tiles, PlanMeta* m) {
   const int64_t need = int64_t(2 * int64_t(nseq) + 1) * (nchunks + 1);
-  if (nseq < 1 || need > kPlanMetaInts || n_tiles > INT32_MAX / 2) return false;
+  if (nseq < 1 || need > kPlanMetaInts || n_tiles > kPlanDeviceMaxTiles) return false;
+  const auto pow2 = [](int x) { return x > 0 && (x & (x - 1)) == 0; };
+  if (!pow2(g.tokens_per_tile) || !pow2(g.block_n)) return false;
+  static_assert(kPlanMaxSeq >= 1, "metadata too small for one sequence");
   m->nseq = nseq;
   m->nchunks = nchunks;
   m->causal = causal != 0;
@@ -104,8 +145,7 @@ bool fill_plan_meta(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_o
 
 hipError_t launch_plan_device(const PlanMeta& m, cpattn_plan_entry* out, hipStream_t stream) {
   if (m.n_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(plan_kernel, dim3(unsigned((m.n_tiles + 255) / 256)), dim3(256), 0, stream, m,
-                     out);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, m, out);
   return hipGetLastError();
 }
 

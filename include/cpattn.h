@@ -386,8 +386,9 @@ cpattn_status cpattn_key_plan_build(const int32_t* cu_seqlens_q, const int32_t* 
  * the plan's bytes, 16-byte aligned) on `stream` from the metadata passed by value.  This is
  * how the forward entry points build their plan when the metadata is small enough:
  * (2 nseq + 1) (nchunks + 1) <= 480 int32 values, e.g. up to 47 sequences at 4 chunks or 119
- * sequences in one chunk; larger metadata is planned on the host and copied.  Returns
- * CPATTN_ERR_UNSUPPORTED for metadata that does not fit (or nseq == 0).  Exposed so the two
+ * sequences in one chunk, and the plan has at most 4096 token tiles (131,072 bf16 query tokens
+ * at 32 per tile); larger calls are planned on the host and copied.  Returns
+ * CPATTN_ERR_UNSUPPORTED for calls beyond these limits (or nseq == 0).  Exposed so the two
  * planners can be compared.
  */
 cpattn_status cpattn_plan_build_device(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

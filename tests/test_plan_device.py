@@ -58,6 +58,27 @@ def test_device_planner_refuses_metadata_beyond_its_argument(gpu_lib):
     assert e.value.status == 2
 
 
+@pytest.mark.parametrize("lengths", [[40000, 37000, 44000], [131072], [4096 * 32 - 40, 3]])
+def test_device_plan_equals_host_plan_up_to_its_tile_limit(gpu_lib, lengths):
+    """Thousands of tiles (the sort runs over padded power-of-two key arrays), three chunks at
+    staggered offsets so that totals tie in long runs."""
+    cu_q = wl.cu_from_lengths(lengths)
+    nseq = len(lengths)
+    q_off = np.full(nseq, 3 * 4096, np.int32)
+    cu_ks = [wl.cu_from_lengths([4096 + 17 * c] * nseq) for c in range(3)]
+    k_offs = [np.full(nseq, 4096 * c + 5 * c, np.int32) for c in range(3)]
+    host, devp = _host_and_device(gpu_lib, cu_q, cu_ks, q_off, k_offs, hq=32, hkv=8, d=128)
+    assert len(host) == sum((n + 31) // 32 for n in lengths) * 3
+    assert host.tobytes() == devp.tobytes()
+
+
+def test_device_planner_refuses_plans_beyond_its_tile_limit(gpu_lib):
+    cu = wl.cu_from_lengths([4096 * 32 + 1])      # 4097 tiles of 32 tokens
+    with pytest.raises(gpu_lib.CpattnError) as e:
+        gpu_lib.cpattn_plan_build_device(cu, [cu], None, None, hq=32, hkv=8, d=128)
+    assert e.value.status == 2
+
+
 def test_device_planned_forward_captured_and_replayed(gpu_lib):
     """cpattn_fwd_chunks with device-planned metadata (the CP4 share of seed 2) captured into
     a graph: every replay, with eager work and synchronisation between replays and inputs
