@@ -11,16 +11,17 @@
 //   bwd_dq      query-stationary, the forward's tiling and its walk over the KV
 //               chunks: per 64-key block S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, then
 //               dQ^T += K^T dS^T; dQ is written once per launch;
-//   bwd_dkdv    key-stationary: a work-group owns 128 keys of one kv head in one
-//               chunk (32 per wave, K and V fragments held in registers) and streams
-//               the query tokens that see them, 64 at a time, for every query head
-//               of the group: S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P,
-//               dK^T += Q^T dS.  One launch covers the key tiles of every chunk,
-//               longest first.  Query blocks that see every key of the tile (all but
-//               the causal diagonal and the ragged end) run in a loop of their own over
-//               a copy of the step without the per-element mask; with one loop body per
-//               case the accumulators stay in the matrix-core registers.
-// Matrix-core mapping: every product is a v_mfma_f32_32x32x16_bf16 whose result
+//   bwd_dkdv    key-stationary: a work-group owns 96 keys of one kv head in one
+//               chunk and streams the query tokens that see them, 32 at a time, for
+//               every query head of the group.  Two waves share 48 keys: one forms
+//               S = Q K^T, P and dV^T += dO^T P and passes P through LDS, the other
+//               forms dP = dO V^T, dS and dK^T += Q^T dS, so each holds one fragment
+//               set and one accumulator (two work-groups per CU).  One launch covers
+//               the key tiles of every chunk, longest first.  Query blocks that see
+//               every key of the tile (all but the causal diagonal and the ragged end)
+//               skip the per-element mask.
+// Matrix-core mapping (bwd_dq; bwd_dkdv describes its own 16x16 tiles below): every
+// product is a v_mfma_f32_32x32x16_bf16 whose result
 // keeps one column index per lane (lane % 32) and 16 row indices per lane, like the
 // forward's S^T tile; the probability-like results (P, dS) are rounded to bf16 and
 // used directly as the B operand of the next product, with the A operand gathered
@@ -39,7 +40,9 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -47,15 +50,16 @@ constexpr int kThreads = 256;              // 4 waves in every backward kernel
 constexpr int BN = kBf16BlockN;            // keys per block of the dQ kernel
 constexpr int QB = kBwdQueryBlock;         // query tokens per block of the dK/dV kernel
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
-static_assert(QB == 64 && BN == 64, "both kernels move 64-row tiles");
+static_assert(QB == 32 && BN == 64, "the dQ kernel moves 64-row tiles, the dK/dV kernel 32-row tiles");
 
-template <int D>
+template <int D, int ROWS = 64>
 struct Tile {
   static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kBytes = 64 * kRowBytes;         // one 64-row bf16 tile
+  static constexpr int kBytes = ROWS * kRowBytes;       // one ROWS-row bf16 tile
   static constexpr int kRowsPerKB = 1024 / kRowBytes;   // rows one wave-wide load fills
   static constexpr int kLoadsPerWave = kBytes / 1024 / 4;
+  static_assert(kLoadsPerWave >= 1, "the 4 waves share a tile's loads");
   // Swizzle for tiles read by rows only (16 consecutive rows, one chunk).
   __device__ static __forceinline__ int swz_rows(int row) {
     return (D == 128) ? (row & 15) : ((row >> 1) & 7);
@@ -70,21 +74,32 @@ struct Tile {
   __device__ static __forceinline__ int off(int row, int c) {
     return row * kRowBytes + ((c ^ (BOTH ? swz_both(row) : swz_rows(row))) << 4);
   }
+  // Swizzle of the dK/dV kernel's 32-row tiles, read by rows (16 consecutive rows, one chunk)
+  // and by 16x16 transpose reads (8 consecutive rows, two adjacent chunks).  For D = 128 it is
+  // a bijection over 16 rows that also puts each of 8 consecutive rows in its own chunk pair
+  // (measured: half the bank-conflict cycles of swz_both on these reads).
+  __device__ static __forceinline__ int swz_pair(int row) {
+    return (D == 128) ? (2 * (row & 7) + ((row >> 3) & 1)) : ((row >> 1) & 7);
+  }
+  __device__ static __forceinline__ int off_pair(int row, int c) {
+    return row * kRowBytes + ((c ^ swz_pair(row)) << 4);
+  }
 };
 
 #if defined(__HIP_DEVICE_COMPILE__)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           int(bytes > 0x7fffffff ? 0x7fffffff : (bytes > 0 ? bytes : 0)),
-                                           kBufferWord3);
+  // clamp to [0, 2^31 - 1] with 32-bit scalar operations (no 64-bit signed compare)
+  const uint64_t u = uint64_t(bytes);
+  const int n = (u >> 63) ? 0 : ((u >> 31) ? 0x7fffffff : int(u));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferWord3);
 }
 
-// Rows [first, first + 64) of a [T, H, D] bf16 tensor for head h, rows past `rows_left` reading
-// as zero, into an LDS tile (this wave's share of the 16 KB / 8 KB).
-template <int D, bool BOTH>
+// Rows [first, first + ROWS) of a [T, H, D] bf16 tensor for head h, rows past `rows_left` reading
+// as zero, into an LDS tile (this wave's quarter of it).
+template <int D, bool BOTH, int ROWS = 64>
 __device__ __forceinline__ void load_tile(const __bf16* base, int64_t first, int h, int nh,
                                           int64_t rows_left, char* lds, int wave, int lane) {
-  using T = Tile<D>;
+  using T = Tile<D, ROWS>;
   const int64_t stride = int64_t(nh) * D * 2;
   const int64_t n = rows_left > 0 ? (rows_left - 1) * stride + D * 2 : 0;
   const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (first * nh + h) * D, n);
@@ -126,16 +141,16 @@ __device__ __forceinline__ void rows_product2(const char* tile_a, const bf16x8* 
   }
 }
 
-// Transposed product: acc^T[d][col] += Tile^T[d][row] * B[row][col] over the tile's 64 rows,
-// the tile's columns gathered by transpose reads, B as bf16 fragments pb[4] (rows 16 kk ..).
-template <int D>
+// Transposed product: acc^T[d][col] += Tile^T[d][row] * B[row][col] over the tile's ROWS rows,
+// the tile's columns gathered by transpose reads, B as bf16 fragments pb[ROWS / 16] (rows 16 kk ..).
+template <int D, int ROWS = 64>
 __device__ __forceinline__ void transposed_product(const char* tile, const bf16x8* pb, int n, int g,
                                                    f32x16* acc) {
-  using T = Tile<D>;
+  using T = Tile<D, ROWS>;
   constexpr int DT = D / 32;
   const int jr = (n & 15) >> 2, qq = n & 3, hh = n >> 4;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
+  for (int kk = 0; kk < ROWS / 16; ++kk) {
     const int row = 16 * kk + 4 * g + jr;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -148,6 +163,20 @@ __device__ __forceinline__ void transposed_product(const char* tile, const bf16x
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], acc[dt], 0, 0, 0);
     }
   }
+}
+
+// Elements 4 h .. 4 h + 3 of a bf16 fragment from four floats, two per conversion.
+__device__ __forceinline__ void set4(bf16x8& f, int h, const float* x) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v = __builtin_bit_cast(s16x8, f);
+  const s16x2 a = __builtin_bit_cast(s16x2, bf16x2{(__bf16)x[0], (__bf16)x[1]});
+  const s16x2 b = __builtin_bit_cast(s16x2, bf16x2{(__bf16)x[2], (__bf16)x[3]});
+  v[4 * h] = a[0];
+  v[4 * h + 1] = a[1];
+  v[4 * h + 2] = b[0];
+  v[4 * h + 3] = b[1];
+  f = __builtin_bit_cast(bf16x8, v);
 }
 
 // bf16 B operand of a transposed product from two 32-row result tiles: rows 16 kk .. 16 kk + 15
@@ -343,157 +372,304 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: key-stationary.  Work-group = one tile of the key plan, all query heads of the
-// kv head's group; wave w owns keys 32 w .. 32 w + 31 of the tile.
+// dK, dV: key-stationary.  Work-group = one tile of the key plan (96 keys of one kv head in
+// one chunk), all query heads of the kv head's group.  The four waves form two pairs; pair p
+// owns keys 48 p .. 48 p + 47 and splits the step's four products between its two waves:
+//   wave A (even):  S = Q K^T, P = exp(S - LSE) (masked), P -> LDS, dV^T += dO^T P;
+//   wave B (odd):   dP = dO V^T, P <- LDS, dS = P (dP - delta), dK^T += Q^T dS.
+// Each wave thus holds one fragment set (K or V) and one accumulator (dV^T or dK^T), about
+// 150 registers for D = 128, so two work-groups share a CU, and every Q or dO fragment read
+// from LDS feeds three 16-key products.  Wave B works one step behind wave A (it needs A's P):
+// the Q / dO / lse / delta tiles rotate through three LDS stages and P through two buffers,
+// and one barrier per step orders everything.
+// Products are v_mfma_f32_16x16x32_bf16 on 16-key tiles nt: a result tile keeps key 16 nt +
+// (lane % 16) in every lane and rows 4 (lane / 16) + r in register r.  For the 32 queries of a
+// step, rows 16 mt + 4 G + r (G = lane / 16) of the two 16-query tiles mt are the eight bf16
+// values of one B operand in (mt, r) order; the matching A operands (dO^T, Q^T) are gathered
+// in the same order by transpose reads.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const ChunkPtrs<__bf16> kv, const __bf16* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta,
     const KeyTile* __restrict__ plan, int hq, int hkv, int tq, float scale, float scale_log2,
     const ChunkPtrs<float> dkv) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using T = Tile<D>;
-  constexpr int KS = D / 16;
-  constexpr int DT = D / 32;
-  constexpr int kStage = 2 * T::kBytes + 512;  // Q tile, dO tile, lse2[64], delta[64]
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+  using T = Tile<D, QB>;
+  constexpr int KS = D / 32;                       // 32-wide k-steps over d
+  constexpr int DT = D / 16;                       // 16-row tiles of d
+  constexpr int NT = kPairKeys / 16;               // 16-key tiles of a pair
+  constexpr int kStage = 2 * T::kBytes + 512;      // Q tile, dO tile, lse2[64], delta[64]
+  constexpr int kPBytes = NT * 1024;               // P of one pair for one step, bf16
+  __shared__ __attribute__((aligned(1024))) char smem[3 * kStage + 2 * 2 * kPBytes];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int n = lane & 31;
-  const int g = lane >> 5;
+  const int i16 = lane & 15;                       // column (key) of a result tile
+  const int G = lane >> 4;                         // 16-lane group
   const int e = blockIdx.x / hkv;
   const int kvh = blockIdx.x - e * hkv;
   const KeyTile pe = plan[e];
-  const __bf16* k = kv.k[pe.chunk];
-  const __bf16* v = kv.v[pe.chunk];
   const int group = hq / hkv;
-  const int key = 32 * wave + n;          // this lane's key within the tile
-  const bool key_ok = key < pe.nrows;
-  const int64_t krow = int64_t(pe.row0) + key;
-
-  // B operands: this lane's key row of K and of V.
-  bf16x8 kf[KS], vf[KS];
-  {
-    const __bf16* kp = k + (krow * hkv + kvh) * D + 8 * g;
-    const __bf16* vp = v + (krow * hkv + kvh) * D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = key_ok ? *reinterpret_cast<const bf16x8*>(kp + 16 * ks) : bf16x8{};
-      vf[ks] = key_ok ? *reinterpret_cast<const bf16x8*>(vp + 16 * ks) : bf16x8{};
-    }
-  }
-  f32x16 dkt[DT], dvt[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) {
-    dkt[i] = f32x16{};
-    dvt[i] = f32x16{};
-  }
+  const int pair = wave >> 1;
+  const bool role_a = (wave & 1) == 0;
+  const int key0 = kPairKeys * pair;               // the pair's first key within the tile
+  char* const pbuf = smem + 3 * kStage + pair * 2 * kPBytes;   // this pair's two P buffers
 
   const int t_first = max(pe.delta, 0);       // first query (within the sequence) to visit
   const int nblk = pe.cost;                   // query blocks per head
   const int total = nblk * group;             // (head, block) steps, head-major
-  auto issue = [&](int step, int stage) {
-    const int hi = step / nblk, j = step - hi * nblk;
-    const int h = kvh * group + hi;
-    const int64_t first = int64_t(pe.q_start) + t_first + int64_t(j) * QB;
-    const int64_t left = int64_t(pe.q_len) - t_first - int64_t(j) * QB;
+  // Loads of step (hi, j): rows t_first + 32 j .. + 31 of query head kvh * group + hi from Q and
+  // dO, and their lse2 (wave 0) and delta (wave 1) values, each through a buffer resource that
+  // ends at the sequence's last query (rows past it read as zero).  The lane offsets within a
+  // tile are the same for every step; the step moves the resource bases.
+  const int64_t row_bytes = int64_t(hq) * D * 2;
+  const int64_t blk_bytes = row_bytes * QB;
+  const int64_t q_first = int64_t(pe.q_start) + t_first;
+  const char* const q0 = reinterpret_cast<const char*>(q + (q_first * hq + kvh * group) * D);
+  const char* const o0 = reinterpret_cast<const char*>(dout + (q_first * hq + kvh * group) * D);
+  const int64_t span0 = int64_t(pe.q_len - t_first - 1) * row_bytes + D * 2;   // bytes of block 0 on
+  const float* const v0 = (wave == 0 ? lse2 : delta) + int64_t(kvh * group) * tq + q_first;
+  const int rows0 = pe.q_len - t_first;
+  int voff[T::kLoadsPerWave];
+#pragma unroll
+  for (int l = 0; l < T::kLoadsPerWave; ++l) {
+    const int row = (wave * T::kLoadsPerWave + l) * T::kRowsPerKB + lane / T::kChunks;
+    voff[l] = row * int(row_bytes) + (((lane % T::kChunks) ^ T::swz_pair(row)) << 4);
+  }
+  auto issue = [&](int hi, int j, int stage) __attribute__((always_inline)) {
     char* s = smem + stage * kStage;
-    load_tile<D, true>(q, first, h, hq, left, s, wave, lane);
-    load_tile<D, true>(dout, first, h, hq, left, s + T::kBytes, wave, lane);
-    if (wave < 2) {  // lse2 (wave 0) and delta (wave 1) of the block's 64 rows, 4 bytes per lane
-      const float* src = (wave == 0 ? lse2 : delta) + int64_t(h) * tq + first;
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(src, left * 4);
+    const int64_t off = int64_t(j) * blk_bytes + hi * (D * 2);
+    const int64_t span = span0 - int64_t(j) * blk_bytes;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q0 + off, span);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o0 + off, span);
+#pragma unroll
+    for (int l = 0; l < T::kLoadsPerWave; ++l) {
+      const int blk = wave * T::kLoadsPerWave + l;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(s + blk * 1024), 16, voff[l], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lds_void*)(s + T::kBytes + blk * 1024), 16, voff[l],
+                                               0, 0, 0);
+    }
+    if (wave < 2) {
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(v0 + int64_t(hi) * tq + int64_t(j) * QB, int64_t(rows0 - j * QB) * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(s + 2 * T::kBytes + 256 * wave), 4,
                                                lane * 4, 0, 0, 0);
     }
   };
-
-  // Query blocks that every query of the tile's 128 keys sees (all but the causal diagonal
-  // and the ragged end): j in [j_full0, j_full1) of every head; the steps of a head run in
-  // three loops (masked, unmasked, masked) so each loop body is one straight copy of the step.
-  const bool tile_full = pe.nrows == kBwdKeysPerTile;
-  // first block whose first query sees the tile's last key, and blocks wholly inside the sequence
-  const int lead = pe.delta + kBwdKeysPerTile - 1 - t_first;
-  const int j_full0 = tile_full ? min(nblk, max(0, (lead + QB - 1) / QB)) : nblk;
-  const int j_full1 = tile_full ? max(j_full0, min(nblk, (pe.q_len - t_first) / QB)) : nblk;
-  auto run_step = [&](int step, auto masked) {
-    const int stage = step & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (step + 1 < total) issue(step + 1, stage ^ 1);
-    const int j = step % nblk;
-    const char* qt = smem + stage * kStage;
-    const char* dt_ = qt + T::kBytes;
-    const float* lse_s = reinterpret_cast<const float*>(qt + 2 * T::kBytes);
-    const float* del_s = lse_s + 64;
-    // Query (within the sequence) of register r of tile tt: t_first + 64 j + 32 tt + 8 (r / 4)
-    // + 4 g + r % 4; visible iff it is < q_len and >= delta + key.
-    const int tb = t_first + j * QB + 4 * g;
-    const int lo = pe.delta + key, hi_excl = pe.q_len;
-    f32x16 s0, s1, p0, p1;
-    // S = Q K^T and dP = dO V^T (rows: tokens)
-    rows_product2<D, true, true>(qt, kf, dt_, vf, n, g, s0, s1, p0, p1);
-    bf16x8 pb[4], db[4];
-    f32x16 ps0, ps1;
-    // Registers 4 i .. 4 i + 3 of tile tt hold rows 32 tt + 8 i + 4 g .. + 3: their lse2 and
-    // delta are one 16-byte LDS read each.  P = exp2(S c - lse2), dS = P (dP - delta).
+  // Steps run head-major: (hi, j) of a step, advanced by one per step, and its LDS stage.
+  struct Cursor {
+    int hi = 0, j = 0, stage = 0;
+    __device__ void next(int nb) {
+      if (++j == nb) { j = 0; ++hi; }
+      stage = stage == 2 ? 0 : stage + 1;
+    }
+  };
+  // Lane-constant parts of the LDS reads.  Row reads (A operand of S and dP): query 16 mt +
+  // i16, d-chunk 4 ks + G.  Transpose reads (A operand of dV^T and dK^T): the lane supplies
+  // query 4 G + jr (+ 16 for elements 4..7) at d columns 16 dt + 4 qq .. + 3 and receives
+  // d = 16 dt + i16 at queries 4 G .. 4 G + 3 (and 16 + 4 G ..).
+  const int jr = i16 >> 2, qq = i16 & 3;
+  auto tr_frag = [&](const char* tile, int dt) __attribute__((always_inline)) {
+    const int c16 = 2 * dt + (qq >> 1);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(tile + T::off_pair(4 * G + jr, c16) + 8 * (qq & 1)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(tile + T::off_pair(16 + 4 * G + jr, c16) + 8 * (qq & 1)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // This lane's row (key 16 nt + i16 of the pair) of a [T, hkv, D] tensor as B operands.
+  auto key_frags = [&](const __bf16* base, bf16x8 (&f)[NT][KS]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 l0 = *reinterpret_cast<const float4*>(lse_s + 8 * i + 4 * g);
-      const float4 l1 = *reinterpret_cast<const float4*>(lse_s + 32 + 8 * i + 4 * g);
-      const float4 d0 = *reinterpret_cast<const float4*>(del_s + 8 * i + 4 * g);
-      const float4 d1 = *reinterpret_cast<const float4*>(del_s + 32 + 8 * i + 4 * g);
-      const float la[4] = {l0.x, l0.y, l0.z, l0.w}, lb[4] = {l1.x, l1.y, l1.z, l1.w};
-      const float da[4] = {d0.x, d0.y, d0.z, d0.w}, dbv[4] = {d1.x, d1.y, d1.z, d1.w};
+    for (int nt = 0; nt < NT; ++nt) {
+      const int key = key0 + 16 * nt + i16;
+      const __bf16* p = base + ((int64_t(pe.row0) + key) * hkv + kvh) * D + 8 * G;
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const int r = 4 * i + k4;
-        float e0 = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -la[k4]));
-        float e1 = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -lb[k4]));
-        if (decltype(masked)::value) {
-          const int t0 = tb + 8 * i + k4, t1 = t0 + 32;
-          e0 = key_ok && t0 >= lo && t0 < hi_excl ? e0 : 0.f;
-          e1 = key_ok && t1 >= lo && t1 < hi_excl ? e1 : 0.f;
+      for (int ks = 0; ks < KS; ++ks)
+        f[nt][ks] = key < pe.nrows ? *reinterpret_cast<const bf16x8*>(p + 32 * ks) : bf16x8{};
+    }
+  };
+  // acc^T tile (dt, nt) holds d = 16 dt + 4 G + r of key 16 nt + i16: fold it into the fp32
+  // gradient rows (times `mul`).
+  auto store_acc = [&](float* base, const f32x4 (&acc)[NT][DT], float mul) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int key = key0 + 16 * nt + i16;
+      if (key < pe.nrows) {
+        float* p = base + ((int64_t(pe.row0) + key) * hkv + kvh) * D + 4 * G;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          float4* c = reinterpret_cast<float4*>(p + 16 * dt);
+          const float4 o = *c;
+          *c = make_float4(fmaf(acc[nt][dt][0], mul, o.x), fmaf(acc[nt][dt][1], mul, o.y),
+                           fmaf(acc[nt][dt][2], mul, o.z), fmaf(acc[nt][dt][3], mul, o.w));
         }
-        ps0[r] = e0;
-        ps1[r] = e1;
-        s0[r] = e0 * (p0[r] - da[k4]);                            // dS
-        s1[r] = e1 * (p1[r] - dbv[k4]);
       }
     }
-    pack_b(ps0, ps1, pb);
-    pack_b(s0, s1, db);
-    transposed_product<D>(dt_, pb, n, g, dvt);   // dV^T += dO^T P
-    transposed_product<D>(qt, db, n, g, dkt);    // dK^T += Q^T dS
   };
 
-  if (total > 0) issue(0, 0);
-  for (int hi = 0; hi < group; ++hi) {
-    const int base = hi * nblk;
-    for (int j = 0; j < j_full0; ++j) run_step(base + j, std::true_type{});
-    for (int j = j_full0; j < j_full1; ++j) run_step(base + j, std::false_type{});
-    for (int j = j_full1; j < nblk; ++j) run_step(base + j, std::true_type{});
-  }
+  if (total > 0) issue(0, 0, 0);
 
-  if (key_ok) {
-    float* kp = const_cast<float*>(dkv.k[pe.chunk]) + (krow * hkv + kvh) * D + 4 * g;
-    float* vp = const_cast<float*>(dkv.v[pe.chunk]) + (krow * hkv + kvh) * D + 4 * g;
+  if (role_a) {
+    bf16x8 kf[NT][KS];
+    key_frags(kv.k[pe.chunk], kf);
+    f32x4 dvt[NT][DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        float4* a = reinterpret_cast<float4*>(kp + 32 * dt + 8 * rq);
-        float4* c = reinterpret_cast<float4*>(vp + 32 * dt + 8 * rq);
-        const float4 ka = *a, va = *c;
-        *a = make_float4(fmaf(dkt[dt][4 * rq], scale, ka.x), fmaf(dkt[dt][4 * rq + 1], scale, ka.y),
-                         fmaf(dkt[dt][4 * rq + 2], scale, ka.z), fmaf(dkt[dt][4 * rq + 3], scale, ka.w));
-        *c = make_float4(dvt[dt][4 * rq] + va.x, dvt[dt][4 * rq + 1] + va.y,
-                         dvt[dt][4 * rq + 2] + va.z, dvt[dt][4 * rq + 3] + va.w);
+      for (int dt = 0; dt < DT; ++dt) dvt[nt][dt] = f32x4{};
+
+    // Blocks that every query of the tile's keys sees in full (all but the causal diagonal and
+    // the ragged end) skip the per-element mask.
+    const bool tile_full = pe.nrows == kBwdKeysPerTile;
+    const int lead = pe.delta + kBwdKeysPerTile - 1 - t_first;
+    const int j_full0 = tile_full ? min(nblk, max(0, (lead + QB - 1) / QB)) : nblk;
+    const int j_full1 = tile_full ? max(j_full0, min(nblk, (pe.q_len - t_first) / QB)) : nblk;
+
+    auto a_step = [&](const Cursor& cur, int pb_sel, auto masked) __attribute__((always_inline)) {
+      const char* qt = smem + cur.stage * kStage;
+      const char* dt_ = qt + T::kBytes;
+      const float* lse_s = reinterpret_cast<const float*>(qt + 2 * T::kBytes);
+      bf16x8 pb[NT];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x4 s[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s[nt] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {   // S = Q K^T, one Q fragment for the three key tiles
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(qt + T::off_pair(16 * mt + i16, 4 * ks + G));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[nt][ks], s[nt], 0, 0, 0);
+        }
+        // Register r holds query t_first + 32 j + 16 mt + 4 G + r of the sequence.
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + 16 * mt + 4 * G);
+        const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+        int lo[NT], hi = 4;
+        if (decltype(masked)::value) {   // visible registers r in [lo, hi) of each key tile
+          const int tb = t_first + cur.j * QB + 16 * mt + 4 * G;
+          hi = min(max(pe.q_len - tb, 0), 4);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const int key = key0 + 16 * nt + i16;
+            lo[nt] = key < pe.nrows ? min(max(pe.delta + key - tb, 0), 4) : 4;
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float p[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(fmaf(s[nt][r], scale_log2, -la[r]));
+            if (decltype(masked)::value) p[r] = (r >= lo[nt] && r < hi) ? p[r] : 0.f;
+          }
+          set4(pb[nt], mt, p);
+        }
+      }
+      char* pw = pbuf + pb_sel * kPBytes + lane * 16;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<bf16x8*>(pw + nt * 1024) = pb[nt];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {     // dV^T += dO^T P, one dO^T fragment for three tiles
+        const bf16x8 a = tr_frag(dt_, dt);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          dvt[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nt], dvt[nt][dt], 0, 0, 0);
+      }
+    };
+
+    // One loop per run of masked or unmasked blocks, so that each loop body holds one copy of
+    // the step.
+    Cursor cur;
+    int s = 0;
+    auto a_iter = [&](auto masked) __attribute__((always_inline)) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      Cursor nx = cur;
+      nx.next(nblk);
+      if (s + 1 < total) issue(nx.hi, nx.j, nx.stage);
+      a_step(cur, s & 1, masked);
+      cur = nx;
+      ++s;
+    };
+    for (int hi = 0; hi < group; ++hi) {
+      for (int j = 0; j < j_full0; ++j) a_iter(std::true_type{});
+      for (int j = j_full0; j < j_full1; ++j) a_iter(std::false_type{});
+      for (int j = j_full1; j < nblk; ++j) a_iter(std::true_type{});
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // wave B's last step
+
+    store_acc(const_cast<float*>(dkv.v[pe.chunk]), dvt, 1.f);
+  } else {
+    bf16x8 vf[NT][KS];
+    key_frags(kv.v[pe.chunk], vf);
+    f32x4 dkt[NT][DT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dkt[nt][dt] = f32x4{};
+
+    // wave A's step one earlier: its tiles are still in stage `cur.stage`, its P in pb_sel
+    auto b_step = [&](const Cursor& cur, int pb_sel) __attribute__((always_inline)) {
+      const char* qt = smem + cur.stage * kStage;
+      const char* dt_ = qt + T::kBytes;
+      const float* del_s = reinterpret_cast<const float*>(qt + 2 * T::kBytes + 256);
+      const char* pr = pbuf + pb_sel * kPBytes + lane * 16;
+      bf16x8 pf[NT], db[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) pf[nt] = *reinterpret_cast<const bf16x8*>(pr + nt * 1024);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x4 p[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) p[nt] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {   // dP = dO V^T, one dO fragment for the three tiles
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(dt_ + T::off_pair(16 * mt + i16, 4 * ks + G));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            p[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vf[nt][ks], p[nt], 0, 0, 0);
+        }
+        const float4 d4 = *reinterpret_cast<const float4*>(del_s + 16 * mt + 4 * G);
+        const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float x[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = float(pf[nt][4 * mt + r]) * (p[nt][r] - dl[r]);
+          set4(db[nt], mt, x);
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {     // dK^T += Q^T dS, one Q^T fragment for three tiles
+        const bf16x8 a = tr_frag(qt, dt);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          dkt[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, db[nt], dkt[nt][dt], 0, 0, 0);
+      }
+    };
+
+    Cursor cur;   // the step wave B works on (one behind the loop counter)
+    Cursor ld;    // the step whose tiles the loop issues
+    for (int s = 0; s <= total; ++s) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (s < total) {
+        ld.next(nblk);
+        if (s + 1 < total) issue(ld.hi, ld.j, ld.stage);
+      }
+      if (s >= 1) {
+        b_step(cur, (s - 1) & 1);
+        cur.next(nblk);
       }
     }
+
+    store_acc(const_cast<float*>(dkv.k[pe.chunk]), dkt, scale);
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }

@@ -47,11 +47,12 @@ void build_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_of
                    cpattn_plan_info* info);
 
 // Backward, key-stationary kernel (dK, dV): a work-group owns kBwdKeysPerTile keys of one
-// kv head (kBwdWaves waves x 32 keys) and streams the query tokens that see them, in blocks
-// of kBwdQueryBlock, for every query head of the kv head's group.
+// kv head (kBwdWaves waves in two pairs, kPairKeys keys a pair) and streams the query tokens
+// that see them, in blocks of kBwdQueryBlock, for every query head of the kv head's group.
 constexpr int kBwdWaves = 4;
-constexpr int kBwdKeysPerTile = 32 * kBwdWaves;
-constexpr int kBwdQueryBlock = 64;
+constexpr int kPairKeys = 48;
+constexpr int kBwdKeysPerTile = kPairKeys * kBwdWaves / 2;
+constexpr int kBwdQueryBlock = 32;
 
 // One tile of the key-stationary plan: kBwdKeysPerTile keys of one sequence in one chunk
 // (the record cpattn_key_plan_build exports).
