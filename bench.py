@@ -2,9 +2,11 @@
 """Benchmark: one CP4 rank's share of a 16,384-token packed budget on one MI355X.
 
 A step is one pass of the whole per-rank hot path on the share's inputs (already
-resident in HBM): host planning, the plan's upload into the caller's workspace, and
-ONE cpattn_fwd_chunks launch that walks every KV chunk of the share with the online
-softmax carried across chunks (the ring loop's merges done in registers).  `value`
+resident in HBM): one cpattn_fwd_chunks call, i.e. its work plan written into the
+caller's workspace (by the library's planner kernel when the metadata is small, as for
+every workload here; else built on the host and copied) and ONE attention launch that
+walks every KV chunk of the share with the online softmax carried across chunks (the
+ring loop's merges done in registers).  `value`
 is the share's algorithmic causal FLOPs (4 * D * Hq per visible query/key pair)
 divided by the step time.  The two other schedules of the same share -- per-chunk
 launches accumulating in the epilogue (cpattn_fwd_chunk_accum), and per-chunk
@@ -48,7 +50,10 @@ ATTN_SOURCE = os.path.join(HERE, "context_ring_attention_amd", "csrc", "attn_fwd
 # HBM bytes per streaming attention launch, from rocprofv3 FETCH_SIZE and WRITE_SIZE runs
 # (scaled by a plain-copy calibration), keyed by workload and the sha256 of the kernel source
 # they were taken on.  Any other pair reports traffic as null until it is profiled again.
-PROFILED_TRAFFIC = {}
+PROFILED_TRAFFIC = {
+    ("cp4_share", "c884679021d39153783aaa25e0a2ceb2fdf2de8e8b23c4291b1b4e3189946f05"): 223533013,
+    ("ctx128k_share", "c884679021d39153783aaa25e0a2ceb2fdf2de8e8b23c4291b1b4e3189946f05"): 3624573408,
+}
 # A pool for the CPU baseline never exceeds one GPU's share of the host's cores.
 MAX_CPU_WORKERS = 16
 
@@ -471,7 +476,7 @@ def main() -> int:
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)",
                      "algorithmic_bytes_per_launch": gg.alg_bytes,
                      "kernel": "attn_fwd_bf16_kernel<128,false> over all chunks (event-timed per "
-                               "cpattn_fwd_chunks call, plan upload included)",
+                               "cpattn_fwd_chunks call, its plan kernel included)",
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
                      "flops_per_launch": flops_step},
         "schedules": schedules,

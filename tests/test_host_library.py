@@ -399,3 +399,18 @@ def test_key_plan_rejects_bad_arguments(lib):
     assert lib.cpattn_key_plan_build(p, p, None, None, 1, 1, 4, 4, 96, 1, None, 0, None) == 2
     buf = ctypes.create_string_buffer(16)
     assert lib.cpattn_key_plan_build(p, p, None, None, 1, 1, 4, 4, 128, 1, buf, 16, None) == 3
+
+
+def test_binding_refuses_host_tensors_before_any_launch():
+    """Every tensor the kernels write through (outputs, gradients, the workspace) must be a
+    CUDA tensor on q's device; the binding checks that before it touches the library, so a
+    host pointer never reaches a kernel."""
+    import torch
+    from context_ring_attention_amd import _binding as b
+    dev0 = torch.device("cuda", 0)
+    with pytest.raises(ValueError, match="CUDA"):
+        b._on_device("out", torch.zeros(4), dev0)
+    with pytest.raises(ValueError, match="CUDA"):
+        b._workspace(torch.zeros(256, dtype=torch.uint8), 16, dev0)
+    with pytest.raises(ValueError, match="CUDA"):
+        b._on_device("dk", torch.zeros((3, 2, 64)), dev0)
