@@ -170,6 +170,26 @@ def cpu_baseline(w, budget_rows: int = 4096, block_rows: int = 256):
 # ---------------------------------------------------------------------------------------------
 # GPU timing helpers.
 
+class LaunchChain:
+    """Durations of the launches of the timed steps from ONE event recorded after each launch
+    (and one at the start): a launch's duration is the time from the previous event to its own.
+    Each event is a marker the GPU stops at; a pair of events around every launch would put two
+    markers between consecutive launches, which idled the GPU ~10 us per step (kernel traces).
+    Consecutive differences tile the timed region, so they sum to the measured step time."""
+
+    def __init__(self, ev, n: int):
+        self.pool = [ev() for _ in range(n)]
+        self.marks = []
+
+    def mark(self, label, stream):
+        e = self.pool[len(self.marks)]
+        e.record(stream)
+        self.marks.append((label, e))
+
+    def durations_ms(self, label):
+        return [a.elapsed_time(b) for (_, a), (lb, b) in zip(self.marks, self.marks[1:]) if lb == label]
+
+
 def timed_steps(step, steps: int, warmup: int, stream, ev):
     """Run `step` warmup times, then time exactly `steps` of them between two events on the
     stream (with the garbage collector frozen: a full collection mid-step idles the GPU)."""
@@ -263,20 +283,19 @@ def time_workload(name, seed, steps, warmup, stream, ev, backward: bool):
     import workloads as wl
     w = wl.make(name, seed)
     gs = [GpuGroup(w, g) for g in w.groups]
-    launch_ev = [[(ev(), ev()) for _ in gs] for _ in range(steps)]
+    chain = LaunchChain(ev, 1 + steps * len(gs))
 
     def step(i):
+        if i is not False and i == 0:
+            chain.mark("start", stream)
         for j, gg in enumerate(gs):
-            if i is not False:
-                launch_ev[i][j][0].record(stream)
             gg.fwd(stream)
             if i is not False:
-                launch_ev[i][j][1].record(stream)
+                chain.mark(j, stream)
 
     ms = timed_steps(step, steps, warmup, stream, ev)
     flops = sum(gg.flops for gg in gs)
-    launch_ms = [sum(r[j][0].elapsed_time(r[j][1]) for r in launch_ev) / steps
-                 for j in range(len(gs))]
+    launch_ms = [sum(chain.durations_ms(j)) / steps for j in range(len(gs))]
     kern_ms = sum(launch_ms)
     tq = sum(gg.tq for gg in gs)
     tk = sum(gg.tk for gg in gs)
@@ -357,30 +376,31 @@ def main() -> int:
     merge_bytes = 3 * (tq * w.hq * w.d * 4 + tq * w.hq * 4)
     n_merge = nch - 1
 
-    attn_ev = {m: [[(ev(), ev()) for _ in g.chunks] for _ in range(args.steps)] for m in cra.MODES}
-    merge_ev = [[(ev(), ev()) for _ in range(n_merge)] for _ in range(args.steps)]
-    spare_attn = [(ev(), ev()) for _ in g.chunks]        # recorded during warm-up, unread
-    spare_merge = [(ev(), ev()) for _ in range(n_merge)]
+    chains = {m: LaunchChain(ev, 1 + args.steps * (nch + n_merge)) for m in cra.MODES}
 
-    def share_step(mode, a_ev, m_ev):
+    def share_step(mode, i):
+        """One step of `mode`; i is the timed step's index, or False during warm-up."""
+        ch = chains[mode] if i is not False else None
+        if ch and i == 0:
+            ch.mark("start", stream)
         if mode == "stream":
-            a_ev[0][0].record(stream)
             gg.fwd(stream)
-            a_ev[0][1].record(stream)
+            if ch:
+                ch.mark("attn", stream)
             return
         for c in range(nch):
             first = c == 0
             out, lse = ((bufs.o_acc, bufs.lse_acc) if first or mode == "accum"
                         else (bufs.o_part, bufs.lse_part))
             fn = cra.cpattn_fwd_chunk if first or mode == "merge" else cra.cpattn_fwd_chunk_accum
-            a_ev[c][0].record(stream)
             fn(q, ks[c], vs[c], cu_q, cu_ks[c], q_off, k_offs[c], True, out=out, lse=lse,
                workspace=bufs.workspace, stream=stream)
-            a_ev[c][1].record(stream)
+            if ch:
+                ch.mark("attn", stream)
             if mode == "merge" and not first:
-                m_ev[c - 1][0].record(stream)
                 cra.cpattn_merge(bufs.o_acc, bufs.lse_acc, bufs.o_part, bufs.lse_part, stream=stream)
-                m_ev[c - 1][1].record(stream)
+                if ch:
+                    ch.mark("merge", stream)
 
     wanted = [m for m in args.schedules.split(",") if m]
     if any(m not in cra.MODES for m in wanted):
@@ -389,12 +409,10 @@ def main() -> int:
     order = [m for m in ("merge", "accum") if m in wanted] + ["stream"]
     schedules = {}
     for mode in order:   # the step's own schedule last, on a warm GPU
-        ms = timed_steps(lambda i, m=mode: share_step(m, spare_attn if i is False else attn_ev[m][i],
-                                                      spare_merge if i is False else merge_ev[i]),
-                         args.steps, args.warmup, stream, ev)
+        ms = timed_steps(lambda i, m=mode: share_step(m, i), args.steps, args.warmup, stream, ev)
         launches = 1 if mode == "stream" else nch
-        a_ms = sum(row[c][0].elapsed_time(row[c][1]) for row in attn_ev[mode]
-                   for c in range(launches)) / (args.steps * launches)
+        a_d = chains[mode].durations_ms("attn")
+        a_ms = sum(a_d) / len(a_d)
         schedules[mode] = {"ms_per_step": round(ms, 4),
                            "tflops": round(flops_step / (ms / 1e3) / 1e12, 2),
                            "attn_launches_per_step": launches,
@@ -405,8 +423,8 @@ def main() -> int:
     attn_tflops = flops_step / (attn_avg_ms / 1e3) / 1e12
 
     timed_merge = "merge" in schedules and n_merge > 0
-    merge_ms = sum(a.elapsed_time(b) for row in merge_ev for a, b in row) if timed_merge else 0.0
-    merge_avg_ms = merge_ms / max(1, args.steps * n_merge)
+    m_d = chains["merge"].durations_ms("merge") if timed_merge else []
+    merge_avg_ms = sum(m_d) / max(1, len(m_d))
     merge_gbs = merge_bytes / (merge_avg_ms / 1e3) / 1e9 if timed_merge else None
     # Reference for the merge's HBM roof: torch's elementwise add over buffers of O's size (two
     # reads and one write, the merge's traffic without the LSE rows), timed the same way.
