@@ -5,10 +5,12 @@
 // chunk, tiles ordered by their total cost over the chunks, longest first, ties in (sequence,
 // tile) order.  One work-group of 1024 threads builds it: the metadata goes to LDS, every
 // thread forms the total of some tiles and packs it with the tile's index into one 64-bit key
-// (INT32_MAX - total above the index, so ascending keys are the plan's order), a bitonic sort
-// in LDS orders the keys, and each thread then writes the entries of some positions of the
-// sorted order.  Every step reads LDS only, so the kernel takes a few microseconds for the
-// plans it accepts (at most kPlanDeviceMaxTiles tiles).
+// (INT32_MAX - total above the index, so ascending keys are the plan's order).  Up to
+// kRankDirect tiles, each thread counts the keys below its own (its rank) and writes its
+// entries there; larger plans bitonic-sort the keys in LDS (log2(n) (log2(n) + 1) / 2
+// barrier-separated stages) and write the entries of the sorted order.  Every step reads LDS
+// only, so the kernel takes a few microseconds for the plans it accepts (at most
+// kPlanDeviceMaxTiles tiles).
 #include "internal.h"
 
 namespace cpattn {
@@ -16,6 +18,8 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanMaxSeq = (kPlanMetaInts / 2 - 1) / 2;   // (2 nseq + 1) * 2 <= kPlanMetaInts
+constexpr int kRankDirect = 256;   // direct ranking: n steps per thread instead of the sort's barriers
+static_assert(kRankDirect <= kPlanThreads, "one thread per tile when ranking directly");
 
 // Metadata accessors over the LDS copy of PlanMeta::v.  Tile and block sizes are powers of two
 // (their logarithms tt_log, bn_log), so the divisions are shifts.
@@ -94,6 +98,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const PlanMeta meta,
     key[t] = k;
   }
   __syncthreads();
+  if (n <= kRankDirect) {   // keys are distinct (the index is part of them)
+    if (tid < n) {
+      const uint64_t mine = key[tid];
+      int rank = 0;
+      for (int u = 0; u < n; ++u) rank += key[u] < mine ? 1 : 0;
+      const int i = seq_of(tid), tb = tid - first[i];
+      for (int c = 0; c < nch; ++c) out[int64_t(rank) * nch + c] = M.entry(i, tb, c);
+    }
+    return;
+  }
   // bitonic sort of key[0, N), ascending
   for (int k = 2; k <= N; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
