@@ -287,13 +287,43 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
 
-  // Block j of chunk c into LDS stage `stage`: K (read by rows and transposed), then V.
-  auto issue = [&](int c, int j, int stage) {
+  // Block j of a chunk into LDS stage `stage`: K (read by rows and transposed), then V, through
+  // buffer resources that end at the sequence's last key of the chunk (rows past it read as
+  // zero).  The lane offsets within a tile are the same for every block; a chunk's K/V bases
+  // and byte span are formed once per chunk, and a block only moves them.
+  const int64_t kv_row_bytes = int64_t(hkv) * D * 2;
+  const int64_t kv_blk_bytes = kv_row_bytes * BN;
+  int voff_k[T::kLoadsPerWave], voff_v[T::kLoadsPerWave];
+#pragma unroll
+  for (int l = 0; l < T::kLoadsPerWave; ++l) {
+    const int row = (wave * T::kLoadsPerWave + l) * T::kRowsPerKB + lane / T::kChunks;
+    const int pc = lane % T::kChunks;
+    voff_k[l] = row * int(kv_row_bytes) + ((pc ^ T::swz_both(row)) << 4);
+    voff_v[l] = row * int(kv_row_bytes) + ((pc ^ T::swz_rows(row)) << 4);
+  }
+  struct ChunkSrc {
+    const char* k;
+    const char* v;
+    int64_t span;   // bytes from the chunk's first key row of this kv head to its last one's end
+  };
+  auto chunk_src = [&](int c) {
+    const int64_t base = (int64_t(tile[c].k_start) * hkv + kvh) * D;
+    return ChunkSrc{reinterpret_cast<const char*>(kv.k[c] + base),
+                    reinterpret_cast<const char*>(kv.v[c] + base),
+                    int64_t(tile[c].k_len - 1) * kv_row_bytes + D * 2};
+  };
+  auto issue = [&](const ChunkSrc& cs, int j, int stage) __attribute__((always_inline)) {
     char* s = smem + stage * kStage;
-    const int64_t first = int64_t(tile[c].k_start) + int64_t(j) * BN;
-    const int64_t left = int64_t(tile[c].k_len) - int64_t(j) * BN;
-    load_tile<D, true>(kv.k[c], first, kvh, hkv, left, s, wave, lane);
-    load_tile<D, false>(kv.v[c], first, kvh, hkv, left, s + T::kBytes, wave, lane);
+    const int64_t off = int64_t(j) * kv_blk_bytes;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(cs.k + off, cs.span - off);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(cs.v + off, cs.span - off);
+#pragma unroll
+    for (int l = 0; l < T::kLoadsPerWave; ++l) {
+      const int blk = wave * T::kLoadsPerWave + l;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(s + blk * 1024), 16, voff_k[l], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(s + T::kBytes + blk * 1024), 16,
+                                               voff_v[l], 0, 0, 0);
+    }
   };
   auto next_chunk = [&](int c) {
     ++c;
@@ -303,10 +333,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   int stage = 0;
   int c = next_chunk(-1);
-  if (c < nchunks) issue(c, 0, 0);
+  if (c < nchunks) issue(chunk_src(c), 0, 0);
   for (; c < nchunks;) {
     const cpattn_plan_entry pe = tile[c];
     const int cn = next_chunk(c);
+    const ChunkSrc src_c = chunk_src(c);
+    const ChunkSrc src_n = cn < nchunks ? chunk_src(cn) : src_c;
     int nblk_w = 0, nfull_w = 0;
     if (rows_w > 0) {
       const int kend = max(0, min(pe.k_len, pe.delta + tok0 + rows_w));
@@ -317,8 +349,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     auto run_block = [&](int j, auto masked) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (j + 1 < nblk) issue(c, j + 1, stage ^ 1);
-      else if (cn < nchunks) issue(cn, 0, stage ^ 1);
+      if (j + 1 < nblk) issue(src_c, j + 1, stage ^ 1);
+      else if (cn < nchunks) issue(src_n, 0, stage ^ 1);
       if (j < nblk_w) {
         const char* kt = smem + stage * kStage;
         const char* vt = kt + T::kBytes;
