@@ -266,3 +266,28 @@ def test_backward_too_many_chunks_is_rejected(gpu_lib):
     with pytest.raises(gpu_lib.CpattnError) as ei:
         gpu_lib.cpattn_bwd_chunks(q, [q] * n, [q] * n, o, lse, q, [0, 4], [[0, 4]] * n)
     assert ei.value.status == 1
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 2, 64)])
+def test_backward_key_tile_edges(gpu_lib, hq, hkv, d):
+    """Key counts one below, at and one above the dK/dV kernel's 16-key tiles, its 48-key wave
+    pairs and its 96-key work-group tiles, with the causal diagonal crossing those boundaries
+    (queries offset so that a sequence's first query sees a few keys of a tile) and query counts
+    around its 32-query blocks."""
+    rng = np.random.default_rng(11 + d)
+    lens_k = [15, 16, 17, 47, 48, 49, 95, 96, 97, 143, 193]
+    lens_q = [31, 32, 33, 40, 64, 65, 96, 97, 100, 130, 161]
+    qo = np.array([0, 3, 16, 20, 47, 1, 60, 0, 90, 15, 100], np.int32)
+    ko = np.zeros(len(lens_k), np.int32)
+    cu_q, cu_k = wl.cu_from_lengths(lens_q), wl.cu_from_lengths(lens_k)
+    q = wl.round_to_bf16(rng.standard_normal((int(cu_q[-1]), hq, d), dtype=np.float32))
+    k = wl.round_to_bf16(rng.standard_normal((int(cu_k[-1]), hkv, d), dtype=np.float32))
+    v = wl.round_to_bf16(rng.standard_normal((int(cu_k[-1]), hkv, d), dtype=np.float32))
+    do = wl.round_to_bf16(rng.standard_normal(q.shape, dtype=np.float32))
+    for causal in (True, False):
+        dq, dk, dv = _run(gpu_lib, q, k, v, do, cu_q, cu_k, qo, ko, causal, 1, rng)
+        rq, rk, rv = attention_bwd_ref(q, k, v, do, cu_q, cu_k, qo, ko, causal)
+        what = f"key-tile edges {hq}/{hkv} d={d} causal={causal}"
+        check_grad(dq, rq, "dq " + what)
+        check_grad(dk, rk, "dk " + what)
+        check_grad(dv, rv, "dv " + what)

@@ -31,3 +31,29 @@ def test_more_than_one_gpu_is_refused():
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                          capture_output=True, text=True, timeout=60)
     assert out.returncode == 2 and "one GPU" in out.stderr
+
+
+def test_launch_chain_durations_tile_the_timed_region():
+    """One event after each launch: a launch's duration runs from the previous event to its
+    own, so the durations of all labels together sum to the span of the chain."""
+    import bench
+
+    clock = [0.0]
+
+    class FakeEvent:
+        def record(self, stream):
+            self.t = clock[0]
+
+        def elapsed_time(self, other):
+            return other.t - self.t
+
+    ch = bench.LaunchChain(FakeEvent, 1 + 3 * 2)
+    ch.mark("start", None)
+    for step in range(3):
+        clock[0] += 5.0          # attention launch
+        ch.mark("attn", None)
+        clock[0] += 1.5          # merge launch
+        ch.mark("merge", None)
+    assert ch.durations_ms("attn") == [5.0, 5.0, 5.0]
+    assert ch.durations_ms("merge") == [1.5, 1.5, 1.5]
+    assert sum(ch.durations_ms("attn")) + sum(ch.durations_ms("merge")) == clock[0]
