@@ -331,23 +331,29 @@ cpattn_status cpattn_fwd_chunks(const void* q, const void* const* ks, const void
 namespace {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Workspace of the backward: the query plan, the key plan (both uploaded by the call), then
-// delta and the log2-scaled LSE (written by the delta kernel), each 256-byte aligned.
+// Workspace of the backward, each region 256-byte aligned: the query plan, the dK/dV launch's
+// key parts (at most two per key tile) and the split tiles' counters (one per split unit,
+// zeroed), all uploaded by the call; delta and the log2-scaled LSE (written by the delta
+// kernel); and the split tiles' partial dK/dV (two slots per split unit), sized for every tile
+// being split.
 struct BwdLayout {
-  int64_t n_q, n_k;                 // entries of the query plan and tiles of the key plan
-  size_t key_plan_at, plan_bytes;   // plans: [0, plan_bytes)
-  size_t delta_at, lse2_at, total;
+  int64_t n_q, n_k, units;          // query plan entries, key tiles, split units (n_k * hkv)
+  size_t key_plan_at, counters_at, plan_bytes;   // uploaded: [0, plan_bytes)
+  size_t delta_at, lse2_at, scratch_at, total;
 };
 
-BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq) {
+BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq, int32_t hkv, int32_t d) {
   BwdLayout l;
   l.n_q = n_q;
   l.n_k = n_k;
+  l.units = n_k * hkv;
   l.key_plan_at = align256(size_t(n_q) * sizeof(cpattn_plan_entry));
-  l.plan_bytes = l.key_plan_at + size_t(n_k) * sizeof(KeyTile);
+  l.counters_at = align256(l.key_plan_at + size_t(2 * n_k) * sizeof(KeyPart));
+  l.plan_bytes = l.counters_at + size_t(l.units) * sizeof(int32_t);
   l.delta_at = align256(l.plan_bytes);
   l.lse2_at = align256(l.delta_at + size_t(tq) * hq * sizeof(float));
-  l.total = std::max<size_t>(256, l.lse2_at + size_t(tq) * hq * sizeof(float));
+  l.scratch_at = align256(l.lse2_at + size_t(tq) * hq * sizeof(float));
+  l.total = std::max<size_t>(256, l.scratch_at + size_t(l.units) * 2 * bwd_part_floats(d) * sizeof(float));
   return l;
 }
 }  // namespace
@@ -355,8 +361,8 @@ BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq) {
 size_t cpattn_bwd_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_q,
                                         const int32_t* cu_seqlens_k, int32_t nchunks, int32_t hq,
                                         int32_t hkv, int32_t d) {
-  (void)d;
   if (nseq < 0 || hq < 1 || hkv < 1 || nchunks < 1 || nchunks > CPATTN_MAX_CHUNKS) return 0;
+  if (d != 64 && d != 128) return 0;
   if (nseq > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return 0;
   for (int32_t i = 0; i < nseq; ++i)
     if (cu_seqlens_q[i + 1] < cu_seqlens_q[i]) return 0;
@@ -366,7 +372,7 @@ size_t cpattn_bwd_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_
         return 0;
   const int64_t tq = nseq > 0 ? cu_seqlens_q[nseq] : 0;
   return bwd_layout(count_tiles(cu_seqlens_q, nseq, kMinTileTokens) * nchunks,
-                    count_key_tiles(cu_seqlens_k, nchunks, nseq), tq, hq).total;
+                    count_key_tiles(cu_seqlens_k, nchunks, nseq), tq, hq, hkv, d).total;
 }
 
 size_t cpattn_bwd_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q,
@@ -429,7 +435,7 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
   const Geometry g = geometry_for(CPATTN_BF16, hq, hkv);
   const int64_t n_qt = count_tiles(cu_seqlens_q, nseq, g.tokens_per_tile);
   const BwdLayout lay = bwd_layout(n_qt * nchunks, count_key_tiles(cu_seqlens_k, nchunks, nseq),
-                                   tq, hq);
+                                   tq, hq, hkv, d);
   if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256))
     return set_error(CPATTN_ERR_WORKSPACE, "workspace of %zu bytes (need %zu, 256-byte aligned)",
                      workspace_bytes, lay.total);
@@ -446,17 +452,32 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
     if (overlaps(in_p[b], in_b[b], ws, lay.total))
       return set_error(CPATTN_ERR_INVALID_ARG, "the workspace must not overlap an input");
 
-  std::vector<char> host(lay.plan_bytes);
+  // Work-groups the GPU runs at once in the dK/dV launch (two per CU), for its balance.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return set_error(CPATTN_ERR_HIP, "cannot read the device's compute-unit count");
+  std::vector<char> host(lay.plan_bytes, 0);   // counters start at zero
   build_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal, g,
                 reinterpret_cast<cpattn_plan_entry*>(host.data()), n_qt, nullptr);
+  std::vector<KeyTile> tiles(size_t(lay.n_k));
   build_key_entries(cu_seqlens_q, cu_seqlens_k, q_pos_offset, k_pos_offset, nchunks, nseq, causal,
-                    reinterpret_cast<KeyTile*>(host.data() + lay.key_plan_at), lay.n_k);
+                    tiles.data(), lay.n_k);
+  int64_t n_split = 0;
+  const int64_t n_parts =
+      build_key_parts(tiles.data(), lay.n_k, hq / hkv, hkv, 2 * cus, lay.n_k,
+                      reinterpret_cast<KeyPart*>(host.data() + lay.key_plan_at), &n_split);
+  if (n_parts * hkv > int64_t(INT32_MAX))
+    return set_error(CPATTN_ERR_UNSUPPORTED, "too many tiles for one launch");
   st = stage_plan(ws, host.data(), host.size(), stream);
   if (st != CPATTN_OK) return st;
   const auto* qplan = reinterpret_cast<const cpattn_plan_entry*>(ws);
-  const auto* kplan = reinterpret_cast<const KeyTile*>(ws + lay.key_plan_at);
+  const auto* kparts = reinterpret_cast<const KeyPart*>(ws + lay.key_plan_at);
+  int* counters = reinterpret_cast<int*>(ws + lay.counters_at);
   float* delta = reinterpret_cast<float*>(ws + lay.delta_at);
   float* lse2 = reinterpret_cast<float*>(ws + lay.lse2_at);
+  float* scratch = reinterpret_cast<float*>(ws + lay.scratch_at);
   ChunkPtrs<__bf16> kv{};
   ChunkPtrs<float> dkv{};
   for (int32_t c = 0; c < nchunks; ++c) {
@@ -470,8 +491,8 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
     err = launch_bwd_dq(q, kv, nchunks, do_, lse, delta, qplan, int(n_qt), head_groups,
                         g.heads_per_tile, hq, hkv, d, int(tq), dq, stream);
   if (err == hipSuccess)
-    err = launch_bwd_dkdv(q, kv, do_, lse2, delta, kplan, int(lay.n_k), hq, hkv, d, int(tq), dkv,
-                          stream);
+    err = launch_bwd_dkdv(q, kv, do_, lse2, delta, kparts, int(n_parts), n_split > 0, hq, hkv, d,
+                          int(tq), dkv, counters, scratch, stream);
   if (err != hipSuccess)
     return set_error(CPATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
   return CPATTN_OK;

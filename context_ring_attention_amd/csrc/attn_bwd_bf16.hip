@@ -420,12 +420,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 // values of one B operand in (mt, r) order; the matching A operands (dO^T, Q^T) are gathered
 // in the same order by transpose reads.
 // ---------------------------------------------------------------------------
-template <int D>
+// kSplit: the launch has split tiles (a build without the split epilogue otherwise, whose
+// register allocation is the leaner one for the main loop).
+template <int D, bool kSplit>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const ChunkPtrs<__bf16> kv, const __bf16* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta,
-    const KeyTile* __restrict__ plan, int hq, int hkv, int tq, float scale, float scale_log2,
-    const ChunkPtrs<float> dkv) {
+    const KeyPart* __restrict__ plan, int hq, int hkv, int tq, float scale, float scale_log2,
+    const ChunkPtrs<float> dkv, int* __restrict__ counters, float* __restrict__ scratch) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = Tile<D, QB>;
   constexpr int KS = D / 32;                       // 32-wide k-steps over d
@@ -434,6 +436,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   constexpr int kStage = 2 * T::kBytes + 512;      // Q tile, dO tile, lse2[64], delta[64]
   constexpr int kPBytes = NT * 1024;               // P of one pair for one step, bf16
   __shared__ __attribute__((aligned(1024))) char smem[3 * kStage + 2 * 2 * kPBytes];
+  __shared__ int arrivals;   // split tiles: parts of this unit that finished before this one
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const int G = lane >> 4;                         // 16-lane group
   const int e = blockIdx.x / hkv;
   const int kvh = blockIdx.x - e * hkv;
-  const KeyTile pe = plan[e];
+  const KeyPart pe = plan[e];
   const int group = hq / hkv;
   const int pair = wave >> 1;
   const bool role_a = (wave & 1) == 0;
@@ -451,7 +454,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
   const int t_first = max(pe.delta, 0);       // first query (within the sequence) to visit
   const int nblk = pe.cost;                   // query blocks per head
-  const int total = nblk * group;             // (head, block) steps, head-major
+  const int h0 = pe.h_begin;                  // the part's query heads of the group: [h0, h1)
+  const int total = nblk * (pe.h_end - h0);   // (head, block) steps, head-major
   // Loads of step (hi, j): rows t_first + 32 j .. + 31 of query head kvh * group + hi from Q and
   // dO, and their lse2 (wave 0) and delta (wave 1) values, each through a buffer resource that
   // ends at the sequence's last query (rows past it read as zero).  The lane offsets within a
@@ -492,7 +496,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   };
   // Steps run head-major: (hi, j) of a step, advanced by one per step, and its LDS stage.
   struct Cursor {
-    int hi = 0, j = 0, stage = 0;
+    int hi, j = 0, stage = 0;
+    __device__ explicit Cursor(int h) : hi(h) {}
     __device__ void next(int nb) {
       if (++j == nb) { j = 0; ++hi; }
       stage = stage == 2 ? 0 : stage + 1;
@@ -524,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   };
   // acc^T tile (dt, nt) holds d = 16 dt + 4 G + r of key 16 nt + i16: fold it into the fp32
   // gradient rows (times `mul`).
-  auto store_acc = [&](float* base, const f32x4 (&acc)[NT][DT], float mul) __attribute__((always_inline)) {
+  auto store_acc_rows = [&](float* base, const f32x4 (&acc)[NT][DT], float mul) __attribute__((always_inline)) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int key = key0 + 16 * nt + i16;
@@ -541,7 +546,41 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     }
   };
 
-  if (total > 0) issue(0, 0, 0);
+  // The end of a part: an unsplit tile folds its accumulator into the gradient rows.  The two
+  // halves of a split tile each store theirs to their slot of the unit's scratch, and then
+  // count their arrival (device scope, after a release fence).  The second to arrive reads the
+  // other's slot (after an acquire fence), adds it, and folds the sum. fp32 addition is
+  // commutative, so the sum is the same whichever half arrives second.  Both roles call this
+  // at the same point, so every wave meets the same barriers.
+  auto finish = [&](float* base, f32x4 (&acc)[NT][DT], float mul) __attribute__((always_inline)) {
+    if (!kSplit || pe.split < 0) {
+      store_acc_rows(base, acc, mul);
+      return;
+    }
+    const int64_t unit = int64_t(pe.split) * hkv + kvh;
+    constexpr int kWaveFloats = NT * DT * 4 * 64;
+    float* mine = scratch + (unit * 2 + pe.part) * bwd_part_floats(D) + wave * kWaveFloats;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4*>(mine + ((nt * DT + dt) * 64 + lane) * 4) = acc[nt][dt];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) arrivals = atomicAdd(counters + unit, 1);
+    __syncthreads();
+    if (arrivals == 0) return;   // the other half folds both
+    __threadfence();
+    const float* other = scratch + (unit * 2 + (pe.part ^ 1)) * bwd_part_floats(D) + wave * kWaveFloats;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        acc[nt][dt] += *reinterpret_cast<const f32x4*>(other + ((nt * DT + dt) * 64 + lane) * 4);
+    store_acc_rows(base, acc, mul);
+  };
+
+  if (total > 0) issue(h0, 0, 0);
 
   if (role_a) {
     bf16x8 kf[NT][KS];
@@ -615,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
     // One loop per run of masked or unmasked blocks, so that each loop body holds one copy of
     // the step.
-    Cursor cur;
+    Cursor cur(h0);
     int s = 0;
     auto a_iter = [&](auto masked) __attribute__((always_inline)) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -627,7 +666,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       cur = nx;
       ++s;
     };
-    for (int hi = 0; hi < group; ++hi) {
+    for (int hi = h0; hi < pe.h_end; ++hi) {
       for (int j = 0; j < j_full0; ++j) a_iter(std::true_type{});
       for (int j = j_full0; j < j_full1; ++j) a_iter(std::false_type{});
       for (int j = j_full1; j < nblk; ++j) a_iter(std::true_type{});
@@ -635,7 +674,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();   // wave B's last step
 
-    store_acc(const_cast<float*>(dkv.v[pe.chunk]), dvt, 1.f);
+    finish(const_cast<float*>(dkv.v[pe.chunk]), dvt, 1.f);
   } else {
     bf16x8 vf[NT][KS];
     key_frags(kv.v[pe.chunk], vf);
@@ -686,8 +725,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       }
     };
 
-    Cursor cur;   // the step wave B works on (one behind the loop counter)
-    Cursor ld;    // the step whose tiles the loop issues
+    Cursor cur(h0);   // the step wave B works on (one behind the loop counter)
+    Cursor ld(h0);    // the step whose tiles the loop issues
     for (int s = 0; s <= total; ++s) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -701,7 +740,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       }
     }
 
-    store_acc(const_cast<float*>(dkv.k[pe.chunk]), dkt, scale);
+    finish(const_cast<float*>(dkv.k[pe.chunk]), dkt, scale);
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -747,20 +786,20 @@ hipError_t launch_bwd_dq(const void* q, const ChunkPtrs<__bf16>& kv, int nchunks
 }
 
 hipError_t launch_bwd_dkdv(const void* q, const ChunkPtrs<__bf16>& kv, const void* do_,
-                           const float* lse2, const float* delta, const KeyTile* plan, int n_tiles,
-                           int hq, int hkv, int d, int tq, const ChunkPtrs<float>& dkv,
-                           hipStream_t stream) {
-  if (n_tiles == 0) return hipSuccess;
-  const dim3 grid(unsigned(n_tiles) * unsigned(hkv));
+                           const float* lse2, const float* delta, const KeyPart* plan, int n_parts,
+                           bool split, int hq, int hkv, int d, int tq, const ChunkPtrs<float>& dkv,
+                           int* counters, float* scratch, hipStream_t stream) {
+  if (n_parts == 0) return hipSuccess;
+  const dim3 grid(unsigned(n_parts) * unsigned(hkv));
   const float scale = 1.0f / sqrtf(float(d));
   const float scale_log2 = scale * 1.4426950408889634f;
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const __bf16*>(q), kv,
                        static_cast<const __bf16*>(do_), lse2, delta, plan, hq, hkv, tq, scale,
-                       scale_log2, dkv);
+                       scale_log2, dkv, counters, scratch);
   };
-  if (d == 128) launch(bwd_dkdv_kernel<128>);
-  else if (d == 64) launch(bwd_dkdv_kernel<64>);
+  if (d == 128) split ? launch(bwd_dkdv_kernel<128, true>) : launch(bwd_dkdv_kernel<128, false>);
+  else if (d == 64) split ? launch(bwd_dkdv_kernel<64, true>) : launch(bwd_dkdv_kernel<64, false>);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

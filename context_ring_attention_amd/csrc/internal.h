@@ -59,9 +59,28 @@ constexpr int kBwdQueryBlock = 32;
 using KeyTile = cpattn_key_tile;
 static_assert(sizeof(KeyTile) == 32, "plan records are 32 bytes");
 
+// One work-group's share of a key tile in the dK/dV launch: query heads [h_begin, h_end) of
+// the kv head's group (the whole group, or half of it when the tile is split).  The two halves
+// of a split tile each leave their partial dK/dV in scratch slot `part` of split unit
+// split * hkv + kvh, and the second to finish adds both and folds them into dK/dV.
+constexpr int kMinSplitSteps = 1024;
+struct KeyPart {
+  int32_t row0, nrows, q_start, q_len, delta, cost, chunk;
+  int32_t h_begin, h_end, split, part, reserved;
+};
+static_assert(sizeof(KeyPart) == 48, "key parts are 48 bytes");
+
 // Number of (chunk, sequence, key block) tiles of the key-stationary plan (cu_k is
 // [nchunks][nseq + 1]).
 int64_t count_key_tiles(const int32_t* cu_k, int32_t nchunks, int32_t nseq);
+
+// The dK/dV launch's parts from the key plan (tiles sorted longest first): a tile of at least
+// kMinSplitSteps steps (cost x group) that exceeds a quarter of the ideal per-slot share of all
+// steps (slots = work-groups the GPU runs at once) is split into its group's two halves of
+// query heads, up to max_split tiles; parts sorted by steps, longest first.  Writes at most 2 n_tiles parts,
+// returns their number and the number of split tiles in *n_split.
+int64_t build_key_parts(const KeyTile* tiles, int64_t n_tiles, int group, int hkv, int slots,
+                        int64_t max_split, KeyPart* out, int64_t* n_split);
 
 // Key-stationary plan over nchunks chunks, sorted by cost, longest first.
 void build_key_entries(const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_off,
@@ -129,10 +148,14 @@ hipError_t launch_bwd_dq(const void* q, const ChunkPtrs<__bf16>& kv, int nchunks
                          const float* lse, const float* delta, const cpattn_plan_entry* plan,
                          int n_tiles, int head_groups, int heads_per_tile, int hq, int hkv, int d,
                          int tq, float* dq, hipStream_t stream);
+// dK/dV over the key parts; counters (one int per split unit, zero on entry) and scratch
+// (two slots of bwd_part_floats(d) floats per split unit) serve the split tiles.
 hipError_t launch_bwd_dkdv(const void* q, const ChunkPtrs<__bf16>& kv, const void* do_,
-                           const float* lse2, const float* delta, const KeyTile* plan, int n_tiles,
-                           int hq, int hkv, int d, int tq, const ChunkPtrs<float>& dkv,
-                           hipStream_t stream);
+                           const float* lse2, const float* delta, const KeyPart* plan, int n_parts,
+                           bool split, int hq, int hkv, int d, int tq, const ChunkPtrs<float>& dkv,
+                           int* counters, float* scratch, hipStream_t stream);
+// Floats of one partial dK/dV slot (a work-group's 96 keys x d, both gradients).
+constexpr int64_t bwd_part_floats(int d) { return int64_t(2) * kBwdKeysPerTile * d; }
 hipError_t launch_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,
                         int64_t t, int hq, int d, hipStream_t stream);
 

@@ -208,8 +208,9 @@ cpattn_status cpattn_fwd_chunks_noalloc(const void* q, const void* const* ks,
  *   metadata  as cpattn_fwd_chunk (host); dtype must be CPATTN_BF16; d in {64, 128}
  *   workspace device, >= cpattn_bwd_workspace_size(...) bytes, 256-byte aligned; it holds
  *             the call's two plans (uploaded as for the forward, see
- *             cpattn_workspace_size), then delta and the log2-scaled LSE, until the
- *             kernels have run; it must not overlap any tensor
+ *             cpattn_workspace_size), delta and the log2-scaled LSE, and the split key
+ *             tiles' partial dK/dV, until the kernels have run; it must not overlap any
+ *             tensor
  * Rows whose LSE is -inf (no visible key in the share) contribute nothing.  No output may
  * overlap an input or another output.  Returns CPATTN_OK, or an error code with nothing
  * enqueued (CPATTN_ERR_UNSUPPORTED for fp32 inputs).
@@ -244,8 +245,15 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Bytes of device workspace one cpattn_bwd_chunk call needs (its query and key plans,
- * delta [hq, Tq] and the LSE in log2 units [hq, Tq], fp32).  Returns 0 for invalid
+ * Bytes of device workspace one cpattn_bwd_chunk call needs. It holds:
+ *   - the query plan and the key plan, with a counter per split key tile;
+ *   - delta [hq, Tq] and the LSE in log2 units [hq, Tq], fp32;
+ *   - scratch for the partial dK/dV of split key tiles. The dK/dV launch splits a long key
+ *     tile between two work-groups (half of the query heads of its GQA group each), so that
+ *     a few long tiles do not leave the launch's last round part-filled. Each half keeps a
+ *     partial of 2 x 96 x d fp32 values here, and the second to finish adds both.
+ * The scratch is sized for every key tile being split: 2 x 2 x 96 x d x 4 bytes per key tile
+ * and kv head, e.g. ~270 MB for the 128K-context CP=4 share (4 x 32,768 keys, one kv head, D = 128). Returns 0 for invalid
  * arguments.
  */
 size_t cpattn_bwd_workspace_size(int32_t nseq, const int32_t* cu_seqlens_q,

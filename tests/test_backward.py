@@ -291,3 +291,28 @@ def test_backward_key_tile_edges(gpu_lib, hq, hkv, d):
         check_grad(dq, rq, "dq " + what)
         check_grad(dk, rk, "dk " + what)
         check_grad(dv, rv, "dv " + what)
+
+
+def test_backward_split_key_tiles_match_and_repeat_bitwise(gpu_lib):
+    """Sequences long enough that the dK/dV launch splits its longest key tiles between two
+    work-groups (half of each GQA group's query heads each, the second to finish adding the
+    two partials): gradients match the oracle, and a second run gives the same bits whichever
+    half finishes second."""
+    import torch
+    rng = np.random.default_rng(21)
+    lens = [3000, 700]          # with 16 query heads per kv head, the first ten key tiles of
+    cu = wl.cu_from_lengths(lens)   # sequence 0 have >= 1,024 (query block, head) steps
+    q = wl.round_to_bf16(rng.standard_normal((int(cu[-1]), 16, 64), dtype=np.float32))
+    k = wl.round_to_bf16(rng.standard_normal((int(cu[-1]), 1, 64), dtype=np.float32))
+    v = wl.round_to_bf16(rng.standard_normal((int(cu[-1]), 1, 64), dtype=np.float32))
+    do = wl.round_to_bf16(rng.standard_normal(q.shape, dtype=np.float32))
+    zeros = np.zeros(len(lens), np.int32)
+    runs = [_run(gpu_lib, q, k, v, do, cu, cu, zeros, zeros, True, 1, np.random.default_rng(0))
+            for _ in range(2)]
+    rq, rk, rv = attention_bwd_ref(q, k, v, do, cu, cu, zeros, zeros, True)
+    check_grad(runs[0][0], rq, "dq split tiles")
+    check_grad(runs[0][1], rk, "dk split tiles")
+    check_grad(runs[0][2], rv, "dv split tiles")
+    for a, b in zip(runs[0], runs[1]):
+        assert np.array_equal(a, b)
+    torch.cuda.synchronize()
