@@ -297,22 +297,32 @@ def test_backward_split_key_tiles_match_and_repeat_bitwise(gpu_lib):
     """Sequences long enough that the dK/dV launch splits its longest key tiles between two
     work-groups (half of each GQA group's query heads each, the second to finish adding the
     two partials): gradients match the oracle, and a second run gives the same bits whichever
-    half finishes second."""
+    half finishes second.  The workspace is filled with NaN before each run, so a partial read
+    before the other half's writes were visible would poison the result."""
     import torch
     rng = np.random.default_rng(21)
     lens = [3000, 700]          # with 16 query heads per kv head, the first ten key tiles of
     cu = wl.cu_from_lengths(lens)   # sequence 0 have >= 1,024 (query block, head) steps
-    q = wl.round_to_bf16(rng.standard_normal((int(cu[-1]), 16, 64), dtype=np.float32))
-    k = wl.round_to_bf16(rng.standard_normal((int(cu[-1]), 1, 64), dtype=np.float32))
-    v = wl.round_to_bf16(rng.standard_normal((int(cu[-1]), 1, 64), dtype=np.float32))
+    hq, hkv, d = 16, 1, 64
+    q = wl.round_to_bf16(rng.standard_normal((int(cu[-1]), hq, d), dtype=np.float32))
+    k = wl.round_to_bf16(rng.standard_normal((int(cu[-1]), hkv, d), dtype=np.float32))
+    v = wl.round_to_bf16(rng.standard_normal((int(cu[-1]), hkv, d), dtype=np.float32))
     do = wl.round_to_bf16(rng.standard_normal(q.shape, dtype=np.float32))
     zeros = np.zeros(len(lens), np.int32)
-    runs = [_run(gpu_lib, q, k, v, do, cu, cu, zeros, zeros, True, 1, np.random.default_rng(0))
-            for _ in range(2)]
+    Q, K, V, DO = dev(q, "bfloat16"), dev(k, "bfloat16"), dev(v, "bfloat16"), dev(do, "bfloat16")
+    o, lse = gpu_lib.cpattn_fwd_chunks(Q, [K], [V], cu, [cu], zeros, [zeros], True)
+    nbytes = gpu_lib.cpattn_bwd_workspace_size_chunks(len(lens), cu, [cu], hq, hkv, d)
+    runs = []
+    for _ in range(2):
+        ws = torch.full(((nbytes + 3) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        dq, dks, dvs = gpu_lib.cpattn_bwd_chunks(Q, [K], [V], o, lse, DO, cu, [cu], zeros,
+                                                 [zeros], True, workspace=ws)
+        torch.cuda.synchronize()
+        runs.append((host(dq), host(dks[0]), host(dvs[0])))
+        del ws
     rq, rk, rv = attention_bwd_ref(q, k, v, do, cu, cu, zeros, zeros, True)
     check_grad(runs[0][0], rq, "dq split tiles")
     check_grad(runs[0][1], rk, "dk split tiles")
     check_grad(runs[0][2], rv, "dv split tiles")
     for a, b in zip(runs[0], runs[1]):
         assert np.array_equal(a, b)
-    torch.cuda.synchronize()
