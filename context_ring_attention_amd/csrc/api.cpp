@@ -337,19 +337,25 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // kernel); and the split tiles' partial dK/dV (two slots per split unit), sized for every tile
 // being split.
 struct BwdLayout {
-  int64_t n_q, n_k, units;          // query plan entries, key tiles, split units (n_k * hkv)
-  size_t key_plan_at, counters_at, plan_bytes;   // uploaded: [0, plan_bytes)
+  int64_t n_q, n_k, units, n_wg;    // query plan entries, key tiles, split units (n_k * hkv),
+                                    // work-groups of the gradient launch (bounds)
+  size_t key_plan_at, counters_at, order_at, plan_bytes;   // uploaded: [0, plan_bytes)
   size_t delta_at, lse2_at, scratch_at, total;
 };
 
-BwdLayout bwd_layout(int64_t n_q, int64_t n_k, int64_t tq, int32_t hq, int32_t hkv, int32_t d) {
+// n_q32: query tiles of 32 tokens (the smallest tile), which bounds the dQ work-groups by
+// n_q32 * hq.
+BwdLayout bwd_layout(int64_t n_q32, int32_t nchunks, int64_t n_k, int64_t tq, int32_t hq,
+                     int32_t hkv, int32_t d) {
   BwdLayout l;
-  l.n_q = n_q;
+  l.n_q = n_q32 * nchunks;
   l.n_k = n_k;
   l.units = n_k * hkv;
-  l.key_plan_at = align256(size_t(n_q) * sizeof(cpattn_plan_entry));
+  l.n_wg = n_q32 * hq + 2 * n_k * hkv;
+  l.key_plan_at = align256(size_t(l.n_q) * sizeof(cpattn_plan_entry));
   l.counters_at = align256(l.key_plan_at + size_t(2 * n_k) * sizeof(KeyPart));
-  l.plan_bytes = l.counters_at + size_t(l.units) * sizeof(int32_t);
+  l.order_at = align256(l.counters_at + size_t(l.units) * sizeof(int32_t));
+  l.plan_bytes = l.order_at + size_t(l.n_wg) * sizeof(uint32_t);
   l.delta_at = align256(l.plan_bytes);
   l.lse2_at = align256(l.delta_at + size_t(tq) * hq * sizeof(float));
   l.scratch_at = align256(l.lse2_at + size_t(tq) * hq * sizeof(float));
@@ -371,7 +377,7 @@ size_t cpattn_bwd_workspace_size_chunks(int32_t nseq, const int32_t* cu_seqlens_
       if (cu_seqlens_k[int64_t(c) * (nseq + 1) + i + 1] < cu_seqlens_k[int64_t(c) * (nseq + 1) + i])
         return 0;
   const int64_t tq = nseq > 0 ? cu_seqlens_q[nseq] : 0;
-  return bwd_layout(count_tiles(cu_seqlens_q, nseq, kMinTileTokens) * nchunks,
+  return bwd_layout(count_tiles(cu_seqlens_q, nseq, kMinTileTokens), nchunks,
                     count_key_tiles(cu_seqlens_k, nchunks, nseq), tq, hq, hkv, d).total;
 }
 
@@ -434,8 +440,8 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
   }
   const Geometry g = geometry_for(CPATTN_BF16, hq, hkv);
   const int64_t n_qt = count_tiles(cu_seqlens_q, nseq, g.tokens_per_tile);
-  const BwdLayout lay = bwd_layout(n_qt * nchunks, count_key_tiles(cu_seqlens_k, nchunks, nseq),
-                                   tq, hq, hkv, d);
+  const BwdLayout lay = bwd_layout(count_tiles(cu_seqlens_q, nseq, kMinTileTokens), nchunks,
+                                   count_key_tiles(cu_seqlens_k, nchunks, nseq), tq, hq, hkv, d);
   if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256))
     return set_error(CPATTN_ERR_WORKSPACE, "workspace of %zu bytes (need %zu, 256-byte aligned)",
                      workspace_bytes, lay.total);
@@ -470,29 +476,65 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
                       reinterpret_cast<KeyPart*>(host.data() + lay.key_plan_at), &n_split);
   if (n_parts * hkv > int64_t(INT32_MAX))
     return set_error(CPATTN_ERR_UNSUPPORTED, "too many tiles for one launch");
+  // The gradient launch's order: dQ tiles (head_groups work-groups each) and dK/dV parts (hkv
+  // work-groups each), both plans already longest first, merged by estimated work per
+  // work-group: a dQ block is 3 products over 64 keys x 128 query rows, a dK/dV step 4
+  // products over 32 queries x 96 keys (in units of 2 D FLOPs).
+  const auto* qents = reinterpret_cast<const cpattn_plan_entry*>(host.data());
+  const auto* kps = reinterpret_cast<const KeyPart*>(host.data() + lay.key_plan_at);
+  auto* order = reinterpret_cast<uint32_t*>(host.data() + lay.order_at);
+  auto dq_work = [&](int64_t e) {
+    int64_t blocks = 0;
+    for (int32_t c = 0; c < nchunks; ++c) blocks += qents[e * nchunks + c].cost;
+    return double(blocks) * 3.0 * kBf16BlockN * kBf16RowsPerWave * kBf16Waves;
+  };
+  auto kv_work = [&](int64_t p) {
+    return double(kps[p].cost) * (kps[p].h_end - kps[p].h_begin) * 4.0 * kBwdQueryBlock *
+           kBwdKeysPerTile;
+  };
+  int64_t n_wg = 0;
+  for (int64_t e = 0, p = 0; e < n_qt || p < n_parts;) {
+    if (p >= n_parts || (e < n_qt && dq_work(e) >= kv_work(p))) {
+      for (int h = 0; h < head_groups; ++h) order[n_wg++] = uint32_t(e * head_groups + h);
+      ++e;
+    } else {
+      for (int h = 0; h < hkv; ++h) order[n_wg++] = kDkdvBit | uint32_t(p * hkv + h);
+      ++p;
+    }
+  }
+  if (n_wg > int64_t(INT32_MAX) || n_qt * head_groups >= int64_t(kDkdvBit) ||
+      n_parts * hkv >= int64_t(kDkdvBit))
+    return set_error(CPATTN_ERR_UNSUPPORTED, "too many tiles for one launch");
   st = stage_plan(ws, host.data(), host.size(), stream);
   if (st != CPATTN_OK) return st;
-  const auto* qplan = reinterpret_cast<const cpattn_plan_entry*>(ws);
-  const auto* kparts = reinterpret_cast<const KeyPart*>(ws + lay.key_plan_at);
-  int* counters = reinterpret_cast<int*>(ws + lay.counters_at);
-  float* delta = reinterpret_cast<float*>(ws + lay.delta_at);
-  float* lse2 = reinterpret_cast<float*>(ws + lay.lse2_at);
-  float* scratch = reinterpret_cast<float*>(ws + lay.scratch_at);
-  ChunkPtrs<__bf16> kv{};
-  ChunkPtrs<float> dkv{};
+  BwdArgs a{};
+  a.q = q;
+  a.dout = do_;
   for (int32_t c = 0; c < nchunks; ++c) {
-    kv.k[c] = static_cast<const __bf16*>(ks[c]);
-    kv.v[c] = static_cast<const __bf16*>(vs[c]);
-    dkv.k[c] = dks[c];
-    dkv.v[c] = dvs[c];
+    a.kv.k[c] = static_cast<const __bf16*>(ks[c]);
+    a.kv.v[c] = static_cast<const __bf16*>(vs[c]);
+    a.dkv.k[c] = dks[c];
+    a.dkv.v[c] = dvs[c];
   }
-  hipError_t err = launch_bwd_delta(do_, o, lse, int(tq), hq, d, delta, lse2, stream);
+  a.lse = lse;
+  a.lse2 = reinterpret_cast<float*>(ws + lay.lse2_at);
+  a.delta = reinterpret_cast<float*>(ws + lay.delta_at);
+  a.qplan = reinterpret_cast<const cpattn_plan_entry*>(ws);
+  a.kplan = reinterpret_cast<const KeyPart*>(ws + lay.key_plan_at);
+  a.counters = reinterpret_cast<int*>(ws + lay.counters_at);
+  a.scratch = reinterpret_cast<float*>(ws + lay.scratch_at);
+  a.dq = dq;
+  a.nchunks = nchunks;
+  a.head_groups = head_groups;
+  a.heads_per_tile = g.heads_per_tile;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.tq = int(tq);
+  hipError_t err = launch_bwd_delta(do_, o, lse, int(tq), hq, d, reinterpret_cast<float*>(ws + lay.delta_at),
+                                    reinterpret_cast<float*>(ws + lay.lse2_at), stream);
   if (err == hipSuccess)
-    err = launch_bwd_dq(q, kv, nchunks, do_, lse, delta, qplan, int(n_qt), head_groups,
-                        g.heads_per_tile, hq, hkv, d, int(tq), dq, stream);
-  if (err == hipSuccess)
-    err = launch_bwd_dkdv(q, kv, do_, lse2, delta, kparts, int(n_parts), n_split > 0, hq, hkv, d,
-                          int(tq), dkv, counters, scratch, stream);
+    err = launch_bwd_fused(a, reinterpret_cast<const uint32_t*>(ws + lay.order_at), int(n_wg),
+                           n_split > 0, d, stream);
   if (err != hipSuccess)
     return set_error(CPATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
   return CPATTN_OK;

@@ -5,22 +5,24 @@
 // LSE (the online softmax of the "Megatron 6D parallelism guide", section 6, leaves
 // exactly that LSE), dP = dO V^T and dS = P * (dP - delta), delta = rowsum(dO * O):
 //   dQ += dS K / sqrt(D),   dK += dS^T Q / sqrt(D),   dV += P^T dO.
-// Three kernels, no atomics (results are deterministic):
+// Two launches, results deterministic (the only atomic is the arrival count of a split key
+// tile, whose two partials are added commutatively):
 //   bwd_delta   delta [hq, Tq] = rowsum(dO * O), HBM-bound, and the LSE in log2 units
-//               (+inf for rows with no visible key) for bwd_dkdv;
-//   bwd_dq      query-stationary, the forward's tiling and its walk over the KV
+//               (+inf for rows with no visible key) for the dK/dV work;
+//   bwd_fused   the dQ and dK/dV work-groups in one grid, interleaved longest first by
+//               the host, so each kind's last round is filled by the other kind:
+//     dQ        query-stationary, the forward's tiling and its walk over the KV
 //               chunks: per 64-key block S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, then
 //               dQ^T += K^T dS^T; dQ is written once per launch;
-//   bwd_dkdv    key-stationary: a work-group owns 96 keys of one kv head in one
+//     dK/dV     key-stationary: a work-group owns 96 keys of one kv head in one
 //               chunk and streams the query tokens that see them, 32 at a time, for
-//               every query head of the group.  Two waves share 48 keys: one forms
-//               S = Q K^T, P and dV^T += dO^T P and passes P through LDS, the other
-//               forms dP = dO V^T, dS and dK^T += Q^T dS, so each holds one fragment
-//               set and one accumulator (two work-groups per CU).  One launch covers
-//               the key tiles of every chunk, longest first.  Query blocks that see
-//               every key of the tile (all but the causal diagonal and the ragged end)
-//               skip the per-element mask.
-// Matrix-core mapping (bwd_dq; bwd_dkdv describes its own 16x16 tiles below): every
+//               the query heads of the group (all, or half for a split tile).  Two
+//               waves share 48 keys: one forms S = Q K^T, P and dV^T += dO^T P and
+//               passes P through LDS, the other forms dP = dO V^T, dS and
+//               dK^T += Q^T dS, so each holds one fragment set and one accumulator (two
+//               work-groups per CU).  Query blocks that see every key of the tile (all
+//               but the causal diagonal and the ragged end) skip the per-element mask.
+// Matrix-core mapping (dQ; the dK/dV body describes its own 16x16 tiles below): every
 // product is a v_mfma_f32_32x32x16_bf16 whose result
 // keeps one column index per lane (lane % 32) and 16 row indices per lane, like the
 // forward's S^T tile; the probability-like results (P, dS) are rounded to bf16 and
@@ -237,9 +239,15 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(const __bf16* __res
 // ---------------------------------------------------------------------------
 // dQ: query-stationary.  Work-group = one tile of the forward's query plan.
 // ---------------------------------------------------------------------------
+// LDS of a dQ work-group: two stages of a K tile (read by rows and transposed) and a V tile.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
-    const __bf16* __restrict__ q, const ChunkPtrs<__bf16> kv, int nchunks,
+constexpr int dq_lds_bytes() { return 2 * 2 * Tile<D>::kBytes; }
+
+// Work-group b of the dQ launch (tile b / head_groups of the query plan, head group
+// b % head_groups), with `smem` its dq_lds_bytes<D>() of LDS.
+template <int D>
+__device__ __forceinline__ void dq_body(
+    int b, char* smem, const __bf16* __restrict__ q, const ChunkPtrs<__bf16>& kv, int nchunks,
     const __bf16* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, const cpattn_plan_entry* __restrict__ plan,
     int head_groups, int heads_per_tile, int hq, int hkv, int tq, float scale, float scale_log2,
@@ -249,14 +257,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int kStage = 2 * T::kBytes;  // K tile (rows and transposed), then V tile (rows)
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31;
   const int g = lane >> 5;
-  const int b = blockIdx.x;
   const int e = b / head_groups;
   const int hg = b - e * head_groups;
   const cpattn_plan_entry* tile = plan + int64_t(e) * nchunks;  // one entry per chunk
@@ -422,12 +428,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // kSplit: the launch has split tiles (a build without the split epilogue otherwise, whose
 // register allocation is the leaner one for the main loop).
+// LDS of a dK/dV work-group: three stages of Q and dO tiles with their lse2 and delta, and
+// two P buffers per wave pair.
+template <int D>
+constexpr int dkdv_lds_bytes() {
+  return 3 * (2 * Tile<D, QB>::kBytes + 512) + 2 * 2 * (kPairKeys / 16) * 1024;
+}
+
+// Work-group wg of the dK/dV launch (part wg / hkv of the key plan, kv head wg % hkv), with
+// `smem` its dkdv_lds_bytes<D>() of LDS and `arrivals` an LDS int.
 template <int D, bool kSplit>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
-    const __bf16* __restrict__ q, const ChunkPtrs<__bf16> kv, const __bf16* __restrict__ dout,
-    const float* __restrict__ lse2, const float* __restrict__ delta,
-    const KeyPart* __restrict__ plan, int hq, int hkv, int tq, float scale, float scale_log2,
-    const ChunkPtrs<float> dkv, int* __restrict__ counters, float* __restrict__ scratch) {
+__device__ __forceinline__ void dkdv_body(
+    int wg, char* smem, int& arrivals, const __bf16* __restrict__ q, const ChunkPtrs<__bf16>& kv,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ delta, const KeyPart* __restrict__ plan, int hq, int hkv, int tq,
+    float scale, float scale_log2, const ChunkPtrs<float>& dkv, int* __restrict__ counters,
+    float* __restrict__ scratch) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = Tile<D, QB>;
   constexpr int KS = D / 32;                       // 32-wide k-steps over d
@@ -435,16 +451,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   constexpr int NT = kPairKeys / 16;               // 16-key tiles of a pair
   constexpr int kStage = 2 * T::kBytes + 512;      // Q tile, dO tile, lse2[64], delta[64]
   constexpr int kPBytes = NT * 1024;               // P of one pair for one step, bf16
-  __shared__ __attribute__((aligned(1024))) char smem[3 * kStage + 2 * 2 * kPBytes];
-  __shared__ int arrivals;   // split tiles: parts of this unit that finished before this one
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int i16 = lane & 15;                       // column (key) of a result tile
   const int G = lane >> 4;                         // 16-lane group
-  const int e = blockIdx.x / hkv;
-  const int kvh = blockIdx.x - e * hkv;
+  const int e = wg / hkv;
+  const int kvh = wg - e * hkv;
   const KeyPart pe = plan[e];
   const int group = hq / hkv;
   const int pair = wave >> 1;
@@ -745,6 +759,33 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// ---------------------------------------------------------------------------
+// The gradient launch: the dQ work-groups and the dK/dV work-groups in one grid, in the
+// longest-first order the host interleaves from both plans (order[b]: dQ work-group, or dK/dV
+// work-group | kDkdvBit), so each kind's last, part-filled round is filled by the other kind.
+// Both bodies run two work-groups per CU; the LDS buffer fits the larger of the two.
+// ---------------------------------------------------------------------------
+template <int D, bool kSplit>
+__global__ __launch_bounds__(kThreads, 2) void bwd_fused_kernel(const BwdArgs a,
+                                                                const uint32_t* __restrict__ order) {
+  constexpr int kLds = dq_lds_bytes<D>() > dkdv_lds_bytes<D>() ? dq_lds_bytes<D>() : dkdv_lds_bytes<D>();
+  __shared__ __attribute__((aligned(1024))) char smem[kLds];
+  __shared__ int arrivals;
+  const uint32_t w = order[blockIdx.x];
+  const float scale = 1.0f / sqrtf(float(D));
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const auto* q = static_cast<const __bf16*>(a.q);
+  const auto* dout = static_cast<const __bf16*>(a.dout);
+  if (w & kDkdvBit) {
+    dkdv_body<D, kSplit>(int(w & ~kDkdvBit), smem, arrivals, q, a.kv, dout, a.lse2, a.delta,
+                         a.kplan, a.hq, a.hkv, a.tq, scale, scale_log2, a.dkv, a.counters,
+                         a.scratch);
+  } else {
+    dq_body<D>(int(w), smem, q, a.kv, a.nchunks, dout, a.lse, a.delta, a.qplan, a.head_groups,
+               a.heads_per_tile, a.hq, a.hkv, a.tq, scale, scale_log2, a.dq);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_delta(const void* do_, const float* o, const float* lse, int tq, int hq,
@@ -766,40 +807,14 @@ hipError_t launch_bwd_delta(const void* do_, const float* o, const float* lse, i
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const void* q, const ChunkPtrs<__bf16>& kv, int nchunks, const void* do_,
-                         const float* lse, const float* delta, const cpattn_plan_entry* plan,
-                         int n_tiles, int head_groups, int heads_per_tile, int hq, int hkv, int d,
-                         int tq, float* dq, hipStream_t stream) {
-  if (n_tiles == 0) return hipSuccess;
-  const dim3 grid(unsigned(n_tiles) * unsigned(head_groups));
-  const float scale = 1.0f / sqrtf(float(d));
-  const float scale_log2 = scale * 1.4426950408889634f;
+hipError_t launch_bwd_fused(const BwdArgs& a, const uint32_t* order, int n_wg, bool split, int d,
+                            hipStream_t stream) {
+  if (n_wg == 0) return hipSuccess;
   auto launch = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const __bf16*>(q), kv,
-                       nchunks, static_cast<const __bf16*>(do_), lse, delta, plan, head_groups,
-                       heads_per_tile, hq, hkv, tq, scale, scale_log2, dq);
+    hipLaunchKernelGGL(kernel, dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, a, order);
   };
-  if (d == 128) launch(bwd_dq_kernel<128>);
-  else if (d == 64) launch(bwd_dq_kernel<64>);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_dkdv(const void* q, const ChunkPtrs<__bf16>& kv, const void* do_,
-                           const float* lse2, const float* delta, const KeyPart* plan, int n_parts,
-                           bool split, int hq, int hkv, int d, int tq, const ChunkPtrs<float>& dkv,
-                           int* counters, float* scratch, hipStream_t stream) {
-  if (n_parts == 0) return hipSuccess;
-  const dim3 grid(unsigned(n_parts) * unsigned(hkv));
-  const float scale = 1.0f / sqrtf(float(d));
-  const float scale_log2 = scale * 1.4426950408889634f;
-  auto launch = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const __bf16*>(q), kv,
-                       static_cast<const __bf16*>(do_), lse2, delta, plan, hq, hkv, tq, scale,
-                       scale_log2, dkv, counters, scratch);
-  };
-  if (d == 128) split ? launch(bwd_dkdv_kernel<128, true>) : launch(bwd_dkdv_kernel<128, false>);
-  else if (d == 64) split ? launch(bwd_dkdv_kernel<64, true>) : launch(bwd_dkdv_kernel<64, false>);
+  if (d == 128) split ? launch(bwd_fused_kernel<128, true>) : launch(bwd_fused_kernel<128, false>);
+  else if (d == 64) split ? launch(bwd_fused_kernel<64, true>) : launch(bwd_fused_kernel<64, false>);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -140,20 +140,35 @@ hipError_t launch_attn_fwd_f32(const float* q, const ChunkPtrs<float>& kv, int n
                                const cpattn_plan_entry* plan, int n_tiles, int hq, int hkv, int d,
                                int tq_total, bool accumulate, float* o, float* lse,
                                hipStream_t stream);
-// Backward launchers: delta = rowsum(dO * O) into delta [hq, tq]; dQ over the query plan
-// (tile-major over nchunks chunks, as the forward's); dK, dV over the key plan.
+// Backward launchers: delta = rowsum(dO * O) into delta [hq, tq] (and the LSE in log2 units);
+// then one gradient launch with dQ over the query plan (tile-major over nchunks chunks, as the
+// forward's) and dK, dV over the key parts.
 hipError_t launch_bwd_delta(const void* do_, const float* o, const float* lse, int tq, int hq,
                             int d, float* delta, float* lse2, hipStream_t stream);
-hipError_t launch_bwd_dq(const void* q, const ChunkPtrs<__bf16>& kv, int nchunks, const void* do_,
-                         const float* lse, const float* delta, const cpattn_plan_entry* plan,
-                         int n_tiles, int head_groups, int heads_per_tile, int hq, int hkv, int d,
-                         int tq, float* dq, hipStream_t stream);
-// dK/dV over the key parts; counters (one int per split unit, zero on entry) and scratch
-// (two slots of bwd_part_floats(d) floats per split unit) serve the split tiles.
-hipError_t launch_bwd_dkdv(const void* q, const ChunkPtrs<__bf16>& kv, const void* do_,
-                           const float* lse2, const float* delta, const KeyPart* plan, int n_parts,
-                           bool split, int hq, int hkv, int d, int tq, const ChunkPtrs<float>& dkv,
-                           int* counters, float* scratch, hipStream_t stream);
+// Arguments of the gradient launch (dQ and dK/dV work-groups in one grid).  qplan holds n_tiles
+// * nchunks entries (tile-major, as the forward's); kplan the key parts; counters (one int per
+// split unit, zero on entry) and scratch (two slots of bwd_part_floats(d) floats per split
+// unit) serve the split key tiles.
+struct BwdArgs {
+  const void* q;
+  const void* dout;
+  ChunkPtrs<__bf16> kv;
+  ChunkPtrs<float> dkv;
+  const float* lse;
+  const float* lse2;
+  const float* delta;
+  const cpattn_plan_entry* qplan;
+  const KeyPart* kplan;
+  int* counters;
+  float* scratch;
+  float* dq;
+  int nchunks, head_groups, heads_per_tile, hq, hkv, tq;
+};
+// order[b] names work-group b of the launch: a dQ work-group (tile * head_groups + head
+// group), or a dK/dV work-group (part * hkv + kv head) with kDkdvBit set.
+constexpr uint32_t kDkdvBit = 0x80000000u;
+hipError_t launch_bwd_fused(const BwdArgs& a, const uint32_t* order, int n_wg, bool split, int d,
+                            hipStream_t stream);
 // Floats of one partial dK/dV slot (a work-group's 96 keys x d, both gradients).
 constexpr int64_t bwd_part_floats(int d) { return int64_t(2) * kBwdKeysPerTile * d; }
 hipError_t launch_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,
