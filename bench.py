@@ -51,8 +51,8 @@ ATTN_SOURCE = os.path.join(HERE, "context_ring_attention_amd", "csrc", "attn_fwd
 # (scaled by a plain-copy calibration), keyed by workload and the sha256 of the kernel source
 # they were taken on.  Any other pair reports traffic as null until it is profiled again.
 PROFILED_TRAFFIC = {
-    ("cp4_share", "c884679021d39153783aaa25e0a2ceb2fdf2de8e8b23c4291b1b4e3189946f05"): 223533013,
-    ("ctx128k_share", "c884679021d39153783aaa25e0a2ceb2fdf2de8e8b23c4291b1b4e3189946f05"): 3624573408,
+    ("cp4_share", "c884679021d39153783aaa25e0a2ceb2fdf2de8e8b23c4291b1b4e3189946f05"): 222803125,
+    ("ctx128k_share", "c884679021d39153783aaa25e0a2ceb2fdf2de8e8b23c4291b1b4e3189946f05"): 3931767285,
 }
 # A pool for the CPU baseline never exceeds one GPU's share of the host's cores.
 MAX_CPU_WORKERS = 16
