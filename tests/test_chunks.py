@@ -199,10 +199,10 @@ def test_cp4_share_stream_full_size_every_row_of_one_head(gpu_lib):
         check(o_h[:, head:head + 1], l_h[head:head + 1], o_ref, l_ref, "bf16", f"cp4 head {head}")
 
 
-def test_plan_ring_reuse_is_exact(gpu_lib):
-    """Plans are staged in a fixed pinned ring that the kernels read in place; after the ring
-    has wrapped around several times (two different packs alternating, ~64 KB of plan each,
-    300 calls), every result is still bitwise the first one of its pack."""
+def test_repeated_calls_are_exact(gpu_lib):
+    """Two different packs called alternately, 150 times each, with the outputs reused: every
+    result is bitwise the first one of its pack (each call plans into its own workspace on the
+    stream; nothing carries over between calls)."""
     import torch
     rng = np.random.default_rng(31)
     packs = []
@@ -214,13 +214,10 @@ def test_plan_ring_reuse_is_exact(gpu_lib):
         vs = [dev(v[r], "bfloat16") for r in rows]
         o, lse = gpu_lib.cpattn_fwd_chunks(Q, ks, vs, cu_q, cus, qo, offs)
         torch.cuda.synchronize()
-        ent, _ = gpu_lib.cpattn_plan_build_chunks(cu_q, cus, qo, offs, hq=32, hkv=8, d=128)
-        packs.append((Q, ks, vs, cu_q, cus, qo, offs, o.clone(), lse.clone(), ent.nbytes))
-    staged = sum(p[-1] for p in packs) * 150
-    assert staged > 2 * (8 << 20), "the calls must wrap the 8 MiB ring"
+        packs.append((Q, ks, vs, cu_q, cus, qo, offs, o.clone(), lse.clone()))
     outs = [(torch.empty_like(p[7]), torch.empty_like(p[8])) for p in packs]
     for it in range(150):
-        for (Q, ks, vs, cu_q, cus, qo, offs, o_ref, l_ref, _), (o, lse) in zip(packs, outs):
+        for (Q, ks, vs, cu_q, cus, qo, offs, o_ref, l_ref), (o, lse) in zip(packs, outs):
             gpu_lib.cpattn_fwd_chunks(Q, ks, vs, cu_q, cus, qo, offs, out=o, lse=lse)
         if it % 10 == 9:
             torch.cuda.synchronize()

@@ -19,6 +19,12 @@ def _host_and_device(cra, cu_q, cu_ks, q_off, k_offs, **kw):
     return host, devp
 
 
+def _tile_tokens(cra, **kw):
+    """Tokens per tile of the forward's geometry for these heads and head size."""
+    cu = wl.cu_from_lengths([1])
+    return cra.cpattn_plan_build_chunks(cu, [cu], None, None, **kw)[1]["tokens_per_tile"]
+
+
 @pytest.mark.parametrize("dtype,hq,hkv", [(0, 32, 8), (0, 8, 1), (0, 6, 3), (0, 4, 2), (0, 5, 5),
                                           (1, 2, 2)])
 def test_device_plan_equals_host_plan_on_random_metadata(gpu_lib, dtype, hq, hkv):
@@ -58,24 +64,32 @@ def test_device_planner_refuses_metadata_beyond_its_argument(gpu_lib):
     assert e.value.status == 2
 
 
-@pytest.mark.parametrize("lengths", [[40000, 37000, 44000], [131072], [4096 * 32 - 40, 3]])
-def test_device_plan_equals_host_plan_up_to_its_tile_limit(gpu_lib, lengths):
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("case", ["three", "one", "limit"])
+def test_device_plan_equals_host_plan_up_to_its_tile_limit(gpu_lib, case, d):
     """Thousands of tiles (the sort runs over padded power-of-two key arrays), three chunks at
-    staggered offsets so that totals tie in long runs."""
+    staggered offsets so that totals tie in long runs; the last case has exactly the planner's
+    limit of 4,096 tiles."""
+    tt = _tile_tokens(gpu_lib, hq=32, hkv=8, d=d)
+    lengths = {"three": [40000, 37000, 44000], "one": [131072], "limit": [4095 * tt - 8, 3]}[case]
     cu_q = wl.cu_from_lengths(lengths)
     nseq = len(lengths)
     q_off = np.full(nseq, 3 * 4096, np.int32)
     cu_ks = [wl.cu_from_lengths([4096 + 17 * c] * nseq) for c in range(3)]
     k_offs = [np.full(nseq, 4096 * c + 5 * c, np.int32) for c in range(3)]
-    host, devp = _host_and_device(gpu_lib, cu_q, cu_ks, q_off, k_offs, hq=32, hkv=8, d=128)
-    assert len(host) == sum((n + 31) // 32 for n in lengths) * 3
+    host, devp = _host_and_device(gpu_lib, cu_q, cu_ks, q_off, k_offs, hq=32, hkv=8, d=d)
+    n_tiles = sum((n + tt - 1) // tt for n in lengths)
+    assert len(host) == n_tiles * 3
+    assert case != "limit" or n_tiles == 4096
     assert host.tobytes() == devp.tobytes()
 
 
-def test_device_planner_refuses_plans_beyond_its_tile_limit(gpu_lib):
-    cu = wl.cu_from_lengths([4096 * 32 + 1])      # 4097 tiles of 32 tokens
+@pytest.mark.parametrize("d", [128, 64])
+def test_device_planner_refuses_plans_beyond_its_tile_limit(gpu_lib, d):
+    tt = _tile_tokens(gpu_lib, hq=32, hkv=8, d=d)
+    cu = wl.cu_from_lengths([4096 * tt + 1])      # 4097 tiles
     with pytest.raises(gpu_lib.CpattnError) as e:
-        gpu_lib.cpattn_plan_build_device(cu, [cu], None, None, hq=32, hkv=8, d=128)
+        gpu_lib.cpattn_plan_build_device(cu, [cu], None, None, hq=32, hkv=8, d=d)
     assert e.value.status == 2
 
 
