@@ -4,8 +4,8 @@ Covers: empty and one-token sequences, zero-length key chunks, chunks wholly
 after the queries (every row empty), causal diagonals inside a tile, ragged
 tails, non-causal mode, both head dims, every GQA grouping the tile geometry
 distinguishes, outputs poisoned before launch (unwritten rows are caught),
-guard bands after the outputs, determinism, and random KV splits merged on the
-GPU against unsplit attention.
+guard bands after the outputs, determinism, random KV splits merged on the
+GPU against unsplit attention, and tensors whose offsets pass 2^32 bytes.
 """
 import numpy as np
 import pytest
@@ -256,3 +256,36 @@ def test_many_sequences_host_planned(gpu_lib, dtype):
     torch.cuda.synchronize()
     check(host(o), host(lse), *attention_ref(q, k, v, cu_q, cu_k, qo, ko), dtype,
           f"200 sequences, host-planned ({dtype})")
+
+
+def test_offsets_beyond_32_bits(gpu_lib):
+    """A 132 x 4,096-token pack at 32/8 heads, D = 128: O holds 2.2e9 elements (8.9 GB, byte
+    offsets past 2^32) and the plan is built on the host (16,896 tiles).  Inputs are drawn on the
+    device from a seeded generator; rows at the start and end of the last sequence (the highest
+    offsets) are checked against the oracle, and the merge of the result with itself at that size
+    against its closed form (the same O, LSE + ln 2)."""
+    import math
+
+    import torch
+    nseq, ln, hq, hkv, d = 132, 4096, 32, 8, 128
+    t = nseq * ln
+    assert t * hq * d > 2**31
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    q = torch.randn((t, hq, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn((t, hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn((t, hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    cu = np.arange(0, t + 1, ln, dtype=np.int32)
+    o, lse = gpu_lib.cpattn_fwd_chunk(q, k, v, cu, cu)
+    torch.cuda.synchronize()
+    s0 = t - ln   # first token of the last sequence
+    ks, vs = host(k[s0:]), host(v[s0:])
+    for lo in (0, ln - 64):   # the sequence's first and last 64 rows
+        rows = slice(s0 + lo, s0 + lo + 64)
+        o_ref, l_ref = attention_ref(host(q[rows]), ks, vs, [0, 64], [0, ln], [lo], [0], True)
+        check(host(o[rows]), host(lse[:, rows]), o_ref, l_ref, "bf16", f"offsets > 2^32, rows {lo}..")
+    del q, k, v
+    o_keep, l_keep = o[s0:].clone(), lse[:, s0:].clone()
+    gpu_lib.cpattn_merge(o, lse, o.clone(), lse.clone())
+    torch.cuda.synchronize()
+    assert torch.allclose(o[s0:], o_keep, rtol=1e-6, atol=1e-7), "merge with itself moved O"
+    assert torch.allclose(lse[:, s0:], l_keep + math.log(2.0), rtol=0, atol=2e-6), "LSE + ln 2"
