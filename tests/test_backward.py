@@ -326,3 +326,31 @@ def test_backward_split_key_tiles_match_and_repeat_bitwise(gpu_lib):
     check_grad(runs[0][2], rv, "dv split tiles")
     for a, b in zip(runs[0], runs[1]):
         assert np.array_equal(a, b)
+
+
+def test_backward_offsets_beyond_32_bits(gpu_lib):
+    """A 132 x 4,096-token pack at 32/8 heads, D = 128 (O, dQ: 2.2e9 elements, 8.9 GB each),
+    inputs drawn on the device from a seeded generator.  The last 64 queries of the last sequence
+    are the only ones that see its last 64 keys (causal), so the oracle on those 64 rows gives
+    their dq exactly and the complete dk, dv of those keys: the highest offsets of every
+    gradient."""
+    import torch
+    nseq, ln, hq, hkv, d = 132, 4096, 32, 8, 128
+    t = nseq * ln
+    assert t * hq * d > 2**31
+    gen = torch.Generator(device="cuda").manual_seed(2025)
+    q = torch.randn((t, hq, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn((t, hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn((t, hkv, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    do = torch.randn((t, hq, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    cu = np.arange(0, t + 1, ln, dtype=np.int32)
+    o, lse = gpu_lib.cpattn_fwd_chunk(q, k, v, cu, cu)
+    dq, dk, dv = gpu_lib.cpattn_bwd_chunk(q, k, v, o, lse, do, cu, cu)
+    torch.cuda.synchronize()
+    s0, lo = t - ln, ln - 64
+    rows = slice(s0 + lo, t)
+    dq_r, dk_r, dv_r = attention_bwd_ref(host(q[rows]), host(k[s0:]), host(v[s0:]), host(do[rows]),
+                                         [0, 64], [0, ln], [lo], [0], True)
+    check_grad(host(dq[rows]), dq_r, "dq, offsets > 2^32")
+    check_grad(host(dk[rows]), dk_r[lo:], "dk, offsets > 2^32")
+    check_grad(host(dv[rows]), dv_r[lo:], "dv, offsets > 2^32")
