@@ -24,8 +24,9 @@ library documents):
      (a multiple of g; the full group starts at 0) whose ranks are in no group
      yet; failing both, a new micro-batch.
 
-Parity unpinned by any printed example (the pages print none): the tests pin it
-with closed forms, invariants and the workload generator's per-sample CP rule.
+The pages print no worked schedule to compare with.  The tests pin this reference
+instead with closed forms, hand-derived placements, invariants checked from the
+constraints above, and the workload generator's per-sample CP rule.
 """
 from __future__ import annotations
 
