@@ -225,8 +225,9 @@ cpattn_status cpattn_bwd_chunk(const void* q, const void* k, const void* v, cons
 
 /*
  * Backward of every KV chunk of a share in one pass (the backward of cpattn_fwd_chunks):
- * delta is formed once, one dQ launch walks all chunks (dq gets the whole share's
- * gradient in one write), and one dK/dV launch covers the key tiles of every chunk.
+ * delta is formed once, then one gradient launch runs the dQ work-groups (each walks all
+ * chunks, so dq gets the whole share's gradient in one write) and the dK/dV work-groups (the
+ * key tiles of every chunk), interleaved longest first.
  * ADDS to dq, dks[c], dvs[c] exactly what nchunks cpattn_bwd_chunk calls would (up to
  * rounding order).
  *   ks, vs      HOST arrays of nchunks device pointers, chunk c [Tk_c, hkv, d] bf16
@@ -246,7 +247,8 @@ cpattn_status cpattn_bwd_chunks(const void* q, const void* const* ks, const void
 
 /*
  * Bytes of device workspace one cpattn_bwd_chunk call needs. It holds:
- *   - the query plan and the key plan, with a counter per split key tile;
+ *   - the query plan, the key plan and the launch order of the gradient launch's
+ *     work-groups, with a counter per split key tile;
  *   - delta [hq, Tq] and the LSE in log2 units [hq, Tq], fp32;
  *   - scratch for the partial dK/dV of split key tiles. The dK/dV launch splits a long key
  *     tile between two work-groups (half of the query heads of its GQA group each), so that
