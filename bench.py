@@ -270,7 +270,7 @@ def time_backward(w, gg, steps, warmup, stream, ev, seed):
             "frac": round(flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "flops_per_step": flops,
             "counted_as": "10 D Hq per visible pair (5 products of the forward's 2 D Hq)",
-            "launches_per_step": "delta, dQ over all chunks, dK/dV over all chunks"}
+            "launches_per_step": "delta, then one gradient launch (dQ and dK/dV work-groups over all chunks)"}
 
 
 def stored_traffic(workload: str):
